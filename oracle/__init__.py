@@ -1,0 +1,35 @@
+"""Plain CPU oracle for the QLoRA NF4 + double-quantisation + LoRA linear path.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or link
+anything in this package: only the test suite, the smoke check and the
+benchmark's CPU-baseline leg use it. It shares no code, tables or constants
+with the HIP library; the two meet only on the seeded inputs.
+
+Every floating-point step is written in float64 (or in float32 where the
+method itself fixes float32 rounding, as the dequantised constants do), in the
+order the pages give, so that a reader can check it against them by eye.
+
+Parity pins: every public function here is pinned by tests under
+``tests/test_oracle_*.py`` against facts fixed outside this module (library
+routines, closed forms, brute force, invariants). The one choice no page
+fixes -- the tail probability ``DELTA`` of the level construction -- is a
+reading and is flagged as such where it is defined.
+"""
+
+from .nf4_oracle import (  # noqa: F401
+    DELTA,
+    NF4_BLOCK,
+    DQ_BLOCK,
+    phi_inv,
+    nf4_levels_f64,
+    nf4_levels,
+    e4m3_decode,
+    e4m3_encode_rne,
+    bf16_round,
+    quantize_nf4_dq,
+    dequant,
+    unpack_codes,
+    storage_bits_per_param,
+    linear_fwd,
+    linear_bwd,
+)

@@ -1,0 +1,73 @@
+"""Pins for the oracle's LoRA linear forward and backward.
+
+The layer is x_out = (W_q + B A) x_in ("QLoRA: Efficient Fine-Tuning of
+Quantized Language Models", mbrenndoerfer.com, section "Low-Rank Adaptation
+(LoRA)"), with tokens as rows and a scale s. Pinned by the merged-weight
+identity, exact directional derivatives (the loss <dY, Y> is linear in each
+of X, A and B separately) and special cases.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+
+
+def _case(M, N, K, r, seed):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((M, K))
+    W = rng.standard_normal((N, K)) * 0.02
+    A = rng.standard_normal((r, K)) * 0.02
+    B = rng.standard_normal((N, r)) * 0.02
+    dY = rng.standard_normal((M, N))
+    return X, W, A, B, dY
+
+
+def test_merged_weight_identity():
+    X, W, A, B, _ = _case(7, 40, 64, 4, 0)
+    s = 2.0
+    Y, T = oracle.linear_fwd(X, W, A, B, s)
+    merged = np.einsum("mk,nk->mn", X, W + s * np.einsum("nj,jk->nk", B, A))
+    np.testing.assert_allclose(Y, merged, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(T, np.einsum("mk,jk->mj", X, A), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("shape", [(16, 256, 256, 8), (1, 96, 128, 3), (5, 33, 64, 1)])
+def test_gradients_are_directional_derivatives(shape):
+    M, N, K, r = shape
+    X, W, A, B, dY = _case(M, N, K, r, 1)
+    s = 0.75
+    dX, dA, dB = oracle.linear_bwd(X, W, A, B, dY, s)
+    loss = lambda X_, A_, B_: float(np.sum(dY * oracle.linear_fwd(X_, W, A_, B_, s)[0]))  # noqa: E731
+    base = loss(X, A, B)
+    rng = np.random.default_rng(2)
+    for _ in range(3):
+        VX, VA, VB = rng.standard_normal(X.shape), rng.standard_normal(A.shape), rng.standard_normal(B.shape)
+        # L is linear in each argument on its own, so a unit step is exact
+        assert abs((loss(X + VX, A, B) - base) - np.sum(dX * VX)) <= 1e-9 * (1 + abs(base))
+        assert abs((loss(X, A + VA, B) - base) - np.sum(dA * VA)) <= 1e-9 * (1 + abs(base))
+        assert abs((loss(X, A, B + VB) - base) - np.sum(dB * VB)) <= 1e-9 * (1 + abs(base))
+    assert dX.shape == X.shape and dA.shape == A.shape and dB.shape == B.shape
+
+
+def test_special_cases():
+    X, W, A, B, dY = _case(6, 20, 64, 4, 3)
+    Y, _ = oracle.linear_fwd(X, W, A, np.zeros_like(B), 1.0)
+    np.testing.assert_allclose(Y, X @ W.T, rtol=1e-13, atol=1e-13)
+    dX, dA, dB = oracle.linear_bwd(X, W, A, np.zeros_like(B), dY, 1.0)
+    assert np.all(dA == 0)
+    dX, dA, dB = oracle.linear_bwd(X, W, np.zeros_like(A), B, dY, 1.0)
+    assert np.all(dB == 0)
+    dX, dA, dB = oracle.linear_bwd(X, W, A, B, dY, 0.0)
+    assert np.all(dA == 0) and np.all(dB == 0)
+    np.testing.assert_allclose(dX, dY @ W, rtol=1e-13, atol=1e-13)
+
+
+def test_single_token_is_dot_products():
+    X, W, A, B, dY = _case(1, 9, 64, 2, 4)
+    s = 0.25
+    Y, T = oracle.linear_fwd(X, W, A, B, s)
+    for n in range(9):
+        t = [sum(X[0, k] * A[j, k] for k in range(64)) for j in range(2)]
+        ref = sum(X[0, k] * W[n, k] for k in range(64)) + s * sum(t[j] * B[n, j] for j in range(2))
+        assert abs(Y[0, n] - ref) <= 1e-13
