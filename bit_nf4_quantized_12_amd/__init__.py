@@ -1,0 +1,247 @@
+"""Python binding of the MI355X (gfx950) NF4 + double-quantisation + LoRA library.
+
+Argument marshalling only: every step runs in the HIP kernels of
+``libqlora.so`` (built in-tree by ``bit_nf4_quantized_12_amd.build``).
+PyTorch provides device memory and the current stream. There is no CPU
+fallback: when the library is missing or fails to load, every call raises.
+
+The function names are those of the C ABI (include/qlora.h):
+
+* ``qlora_nf4_levels()``
+* ``qlora_quantize_nf4_dq(w)``
+* ``qlora_dequant(codes, c2, c1, n, dtype)``
+* ``qlora_linear_workspace_bytes(M, N, K, r)``
+* ``qlora_linear_fwd(W, X, A, B, scale, ...)``
+* ``qlora_linear_bwd(W, X, A, B, dY, T, scale, ...)``
+"""
+
+import ctypes
+import os
+import threading
+from collections import namedtuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlora.so")
+
+QLORA_F32 = 0
+QLORA_BF16 = 1
+
+_lock = threading.Lock()
+_lib = None
+
+
+class QloraError(RuntimeError):
+    """A library call returned a non-zero status."""
+
+
+class _Weight(ctypes.Structure):
+    _fields_ = [
+        ("codes", ctypes.c_void_p),
+        ("c2_fp8", ctypes.c_void_p),
+        ("c1", ctypes.c_void_p),
+        ("rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64),
+    ]
+
+
+def load_library(path=LIB_PATH):
+    """Load libqlora.so (once). Raises ImportError if it is missing or broken."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise ImportError(
+                f"{path} not found: build it with `python -m bit_nf4_quantized_12_amd.build`")
+        lib = ctypes.CDLL(path)
+        vp, i64, f32, sz, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_int
+        sig = {
+            "qlora_nf4_levels": ([ctypes.POINTER(ctypes.c_float)], i32),
+            "qlora_quantize_nf4_dq": ([vp, i64, vp, vp, vp, vp], i32),
+            "qlora_dequant": ([vp, vp, vp, i64, i32, vp, vp], i32),
+            "qlora_linear_workspace_bytes": ([i64, i64, i64, i64], sz),
+            "qlora_linear_fwd": ([ctypes.POINTER(_Weight), vp, vp, vp, i64, i64, f32, vp, vp, vp, sz, vp], i32),
+            "qlora_linear_bwd": ([ctypes.POINTER(_Weight), vp, vp, vp, vp, vp, i64, i64, f32, vp, vp, vp, vp, sz, vp], i32),
+            "qlora_status_string": ([i32], ctypes.c_char_p),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = lib
+        return lib
+
+
+def _check(status):
+    if status != 0:
+        msg = load_library().qlora_status_string(status).decode()
+        raise QloraError(f"qlora status {status}: {msg}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+NF4Weight = namedtuple("NF4Weight", ["codes", "c2", "c1", "rows", "cols"])
+NF4Weight.__doc__ = "Stored NF4 + DQ weight [rows, cols]: device tensors codes (uint8), c2 (uint8), c1 (float32)."
+
+
+def storage_sizes(n):
+    """(bytes of codes, bytes of c2, number of c1 floats) for n weights."""
+    nb = -(-n // 64)
+    return -(-n // 2), nb, -(-nb // 256)
+
+
+def qlora_nf4_levels():
+    """The 16 NF4 levels (float32, ascending) as a CPU tensor."""
+    out = (ctypes.c_float * 16)()
+    _check(load_library().qlora_nf4_levels(out))
+    return torch.tensor(list(out), dtype=torch.float32)
+
+
+def qlora_quantize_nf4_dq(w, out=None):
+    """Quantise bf16 weights (any shape, C order) -> (codes, c2, c1) device tensors.
+
+    ``out`` may supply preallocated (codes, c2, c1) tensors of the right sizes.
+    """
+    _need(w, torch.bfloat16, "w")
+    n = w.numel()
+    nc, nb, ng = storage_sizes(n)
+    if out is None:
+        dev = w.device
+        codes = torch.empty(nc, dtype=torch.uint8, device=dev)
+        c2 = torch.empty(nb, dtype=torch.uint8, device=dev)
+        c1 = torch.empty(ng, dtype=torch.float32, device=dev)
+    else:
+        codes, c2, c1 = out
+    lib = load_library()
+    _check(lib.qlora_quantize_nf4_dq(_ptr(w), n, _ptr(codes), _ptr(c2), _ptr(c1), _stream(w.device)))
+    return codes, c2, c1
+
+
+def quantize_weight(w):
+    """Quantise a 2-D bf16 weight [N, K] into an NF4Weight."""
+    if w.dim() != 2:
+        raise ValueError("weight must be 2-D [out, in]")
+    codes, c2, c1 = qlora_quantize_nf4_dq(w)
+    return NF4Weight(codes, c2, c1, w.shape[0], w.shape[1])
+
+
+def qlora_dequant(codes, c2, c1, n, dtype=torch.float32, out=None):
+    """Dequantise n stored weights to float32 (W^) or bfloat16 (W~)."""
+    _need(codes, torch.uint8, "codes")
+    _need(c2, torch.uint8, "c2")
+    _need(c1, torch.float32, "c1")
+    code = {torch.float32: QLORA_F32, torch.bfloat16: QLORA_BF16}.get(dtype)
+    if code is None:
+        raise TypeError("dtype must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty(n, dtype=dtype, device=codes.device)
+    _check(load_library().qlora_dequant(_ptr(codes), _ptr(c2), _ptr(c1), n, code, _ptr(out),
+                                        _stream(codes.device)))
+    return out
+
+
+def qlora_linear_workspace_bytes(M, N, K, r):
+    return int(load_library().qlora_linear_workspace_bytes(M, N, K, r))
+
+
+def _weight_struct(W):
+    _need(W.codes, torch.uint8, "W.codes")
+    _need(W.c2, torch.uint8, "W.c2")
+    _need(W.c1, torch.float32, "W.c1")
+    return _Weight(W.codes.data_ptr(), W.c2.data_ptr(), W.c1.data_ptr(), W.rows, W.cols)
+
+
+def _workspace(M, N, K, r, device, workspace):
+    need = qlora_linear_workspace_bytes(M, N, K, r)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def qlora_linear_fwd(W, X, A, B, scale, save_T=True, Y=None, T=None, workspace=None):
+    """Y = X W~^T + scale (X A^T) B^T (bf16). Returns (Y, T) with T float32 [M, r] or None."""
+    _need(X, torch.bfloat16, "X")
+    _need(A, torch.bfloat16, "A")
+    _need(B, torch.bfloat16, "B")
+    M, K = X.shape
+    r = A.shape[0]
+    if K != W.cols or A.shape[1] != K or B.shape != (W.rows, r):
+        raise ValueError("shape mismatch: X [M, K], A [r, K], B [N, r], W [N, K]")
+    dev = X.device
+    if Y is None:
+        Y = torch.empty((M, W.rows), dtype=torch.bfloat16, device=dev)
+    if save_T and T is None:
+        T = torch.empty((M, r), dtype=torch.float32, device=dev)
+    if not save_T:
+        T = None
+    ws = _workspace(M, W.rows, K, r, dev, workspace)
+    w = _weight_struct(W)
+    _check(load_library().qlora_linear_fwd(ctypes.byref(w), _ptr(X), _ptr(A), _ptr(B), M, r,
+                                           float(scale), _ptr(Y), _ptr(T), _ptr(ws), ws.numel(),
+                                           _stream(dev)))
+    return Y, T
+
+
+def qlora_linear_bwd(W, X, A, B, dY, T, scale, need_dX=True, dX=None, dA=None, dB=None,
+                     workspace=None):
+    """Gradients (dX or None, dA, dB), all bf16, of qlora_linear_fwd for dY."""
+    for t, name in ((X, "X"), (A, "A"), (B, "B"), (dY, "dY")):
+        _need(t, torch.bfloat16, name)
+    if T is not None:
+        _need(T, torch.float32, "T")
+    M, K = X.shape
+    r = A.shape[0]
+    N = W.rows
+    if dY.shape != (M, N) or K != W.cols or A.shape[1] != K or B.shape != (N, r):
+        raise ValueError("shape mismatch")
+    dev = X.device
+    if need_dX and dX is None:
+        dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    if not need_dX:
+        dX = None
+    if dA is None:
+        dA = torch.empty((r, K), dtype=torch.bfloat16, device=dev)
+    if dB is None:
+        dB = torch.empty((N, r), dtype=torch.bfloat16, device=dev)
+    ws = _workspace(M, N, K, r, dev, workspace)
+    w = _weight_struct(W)
+    _check(load_library().qlora_linear_bwd(ctypes.byref(w), _ptr(X), _ptr(A), _ptr(B), _ptr(dY),
+                                           _ptr(T), M, r, float(scale), _ptr(dX), _ptr(dA),
+                                           _ptr(dB), _ptr(ws), ws.numel(), _stream(dev)))
+    return dX, dA, dB
+
+
+class LoRALinear4bitFunction(torch.autograd.Function):
+    """Autograd wrapper: frozen NF4 weight, trainable A and B, input X."""
+
+    @staticmethod
+    def forward(ctx, X, A, B, W, scale):
+        Y, T = qlora_linear_fwd(W, X.contiguous(), A.contiguous(), B.contiguous(), scale)
+        ctx.save_for_backward(X, A, B, T)
+        ctx.W = W
+        ctx.scale = scale
+        return Y
+
+    @staticmethod
+    def backward(ctx, dY):
+        X, A, B, T = ctx.saved_tensors
+        dX, dA, dB = qlora_linear_bwd(ctx.W, X, A, B, dY.contiguous(), T, ctx.scale,
+                                      need_dX=ctx.needs_input_grad[0])
+        return dX, dA, dB, None, None

@@ -1,0 +1,299 @@
+// C ABI of the library: argument validation (before any HIP call),
+// workspace layout and the launch sequence of each entry point.
+// The operations themselves are defined in include/qlora.h.
+#include <algorithm>
+#include <cmath>
+#include <new>
+
+#include "../../include/qlora.h"
+#include "launch.hpp"
+
+
+using namespace qlora;
+
+namespace {
+
+constexpr int kGemvMaxM = 16;
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+inline int clampi(int64_t v, int64_t lo, int64_t hi) { return (int)(v < lo ? lo : (v > hi ? hi : v)); }
+
+// Reduction splits. Each aims at a few hundred workgroups on 256 CUs.
+inline int proj_splits(int64_t M, int64_t Kr) {
+  const int64_t max_split = std::max<int64_t>(1, Kr / 128);
+  if (M <= kGemvMaxM) return clampi(Kr / 256, 1, std::min<int64_t>(64, max_split));
+  return clampi(cdiv(256, cdiv(M, 64)), 1, std::min<int64_t>(32, max_split));
+}
+inline int gemv_splits(int64_t N, int64_t K) {
+  return clampi(cdiv(512, cdiv(N, 64)), 1, std::max<int64_t>(1, K / 512));
+}
+inline int grad_splits(int64_t M, int64_t C, int64_t rp) {
+  const int64_t wgs = cdiv(C, 128) * cdiv(rp, 64);
+  return clampi(cdiv(512, wgs), 1, std::max<int64_t>(1, cdiv(M, 128)));
+}
+
+struct Layout {
+  // byte offsets into the workspace; kNone when unused
+  size_t partT = 0, T32 = 0, Ts = 0, Bpad = 0, gemvp = 0;            // forward
+  size_t Bt = 0, At = 0, partU = 0, U32 = 0, Us = 0, gpart = 0;      // backward
+  size_t fwd_total = 0, bwd_total = 0;
+  int tsplit = 1, gsplit = 1, usplit = 1, sA = 1, sB = 1;
+};
+
+Layout plan(int64_t M, int64_t N, int64_t K, int64_t r) {
+  Layout L;
+  const int64_t rp = cdiv(r, 32) * 32;
+  // forward
+  L.tsplit = proj_splits(M, K);
+  size_t o = 0;
+  L.partT = o; o = al256(o + (size_t)L.tsplit * M * rp * 4);
+  L.T32 = o;   o = al256(o + (size_t)M * r * 4);
+  L.Ts = o;    o = al256(o + (size_t)M * rp * 2);
+  L.Bpad = o;  o = al256(o + (rp != r ? (size_t)N * rp * 2 : 0));
+  L.gsplit = gemv_splits(N, K);
+  L.gemvp = o; o = al256(o + (M <= kGemvMaxM ? (size_t)L.gsplit * M * N * 4 : 0));
+  L.fwd_total = o;
+  // backward (T recompute reuses the forward region [partT, Ts))
+  L.usplit = proj_splits(M, N);
+  o = L.Bpad;  // T partials, T32 and Ts precede
+  L.Bt = o;    o = al256(o + (size_t)r * N * 2);
+  L.At = o;    o = al256(o + (size_t)K * rp * 2);
+  L.partU = o; o = al256(o + (size_t)L.usplit * M * rp * 4);
+  L.U32 = o;   o = al256(o + (size_t)M * r * 4);
+  L.Us = o;    o = al256(o + (size_t)M * rp * 2);
+  L.sA = grad_splits(M, K, rp);
+  L.sB = grad_splits(M, N, rp);
+  L.gpart = o;
+  o = al256(o + std::max((size_t)L.sA * rp * K * 4, (size_t)L.sB * rp * N * 4));
+  L.bwd_total = o;
+  return L;
+}
+
+int check_linear(const qlora_nf4_weight* W, const void* X, const void* A, const void* B,
+                 int64_t M, int64_t r, float scale, const void* ws, size_t ws_bytes) {
+  if (!W || !X || !A || !B) return QLORA_ERR_NULL;
+  if (!W->codes || !W->c2_fp8 || !W->c1) return QLORA_ERR_NULL;
+  const int64_t N = W->rows, K = W->cols;
+  if (M < 1 || N < 1 || K < 64 || (K % 64) != 0) return QLORA_ERR_SHAPE;
+  if (r < 1 || r > 256) return QLORA_ERR_SHAPE;
+  if (M * std::max(N, K) >= (int64_t(1) << 31) || N * K >= (int64_t(1) << 40)) return QLORA_ERR_SHAPE;
+  if (!std::isfinite(scale)) return QLORA_ERR_UNSUPPORTED;
+  if (!aligned(W->codes, 16) || !aligned(W->c2_fp8, 16) || !aligned(W->c1, 4)) return QLORA_ERR_ALIGN;
+  if (!aligned(X, 16) || !aligned(A, 16) || !aligned(B, 16)) return QLORA_ERR_ALIGN;
+  if (!ws) return QLORA_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return QLORA_ERR_ALIGN;
+  (void)ws_bytes;
+  return QLORA_OK;
+}
+
+#define QLORA_TRY(expr)                                \
+  do {                                                 \
+    if ((expr) != hipSuccess) return QLORA_ERR_DEVICE; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int qlora_nf4_levels(float out[16]) {
+  if (!out) return QLORA_ERR_NULL;
+  try {
+    if (tables_status() != 0) return QLORA_ERR_UNSUPPORTED;
+    const Levels& lv = host_levels();
+    for (int i = 0; i < 16; ++i) out[i] = lv.q[i];
+    return QLORA_OK;
+  } catch (...) {
+    return QLORA_ERR_DEVICE;
+  }
+}
+
+const char* qlora_status_string(int status) {
+  switch (status) {
+    case QLORA_OK: return "ok";
+    case QLORA_ERR_NULL: return "null pointer argument";
+    case QLORA_ERR_SHAPE: return "size out of range or inconsistent";
+    case QLORA_ERR_ALIGN: return "pointer not aligned (16 bytes; 4 for c1/T; 256 for workspace)";
+    case QLORA_ERR_UNSUPPORTED: return "unsupported mode or value";
+    case QLORA_ERR_WORKSPACE: return "workspace missing or too small";
+    case QLORA_ERR_DEVICE: return "HIP call failed";
+    default: return "unknown status";
+  }
+}
+
+int qlora_quantize_nf4_dq(const void* w_bf16, int64_t n, uint8_t* codes, uint8_t* c2_fp8,
+                          float* c1, void* stream) {
+  if (!w_bf16 || !codes || !c2_fp8 || !c1) return QLORA_ERR_NULL;
+  if (n < 1) return QLORA_ERR_SHAPE;
+  if (!aligned(w_bf16, 16) || !aligned(codes, 16) || !aligned(c2_fp8, 16) || !aligned(c1, 4))
+    return QLORA_ERR_ALIGN;
+  try {
+    if (tables_status() != 0) return QLORA_ERR_UNSUPPORTED;
+    QLORA_TRY(launch_quantize(w_bf16, n, codes, c2_fp8, c1, (hipStream_t)stream));
+    return QLORA_OK;
+  } catch (...) {
+    return QLORA_ERR_DEVICE;
+  }
+}
+
+int qlora_dequant(const uint8_t* codes, const uint8_t* c2_fp8, const float* c1, int64_t n,
+                  int out_dtype, void* out, void* stream) {
+  if (!codes || !c2_fp8 || !c1 || !out) return QLORA_ERR_NULL;
+  if (n < 1) return QLORA_ERR_SHAPE;
+  if (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16) return QLORA_ERR_UNSUPPORTED;
+  if (!aligned(codes, 16) || !aligned(c2_fp8, 16) || !aligned(c1, 4) || !aligned(out, 16))
+    return QLORA_ERR_ALIGN;
+  try {
+    if (tables_status() != 0) return QLORA_ERR_UNSUPPORTED;
+    QLORA_TRY(launch_dequant(codes, c2_fp8, c1, n, out_dtype == QLORA_BF16, out, (hipStream_t)stream));
+    return QLORA_OK;
+  } catch (...) {
+    return QLORA_ERR_DEVICE;
+  }
+}
+
+size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
+  if (M < 1 || N < 1 || K < 64 || (K % 64) != 0 || r < 1 || r > 256) return 0;
+  if (M * std::max(N, K) >= (int64_t(1) << 31)) return 0;
+  const Layout L = plan(M, N, K, r);
+  return std::max(L.fwd_total, L.bwd_total);
+}
+
+int qlora_linear_fwd(const qlora_nf4_weight* W, const void* X, const void* A, const void* B,
+                     int64_t M, int64_t r, float scale, void* Y, float* T_save, void* ws,
+                     size_t ws_bytes, void* stream) {
+  int st = check_linear(W, X, A, B, M, r, scale, ws, ws_bytes);
+  if (st != QLORA_OK) return st;
+  if (!Y) return QLORA_ERR_NULL;
+  if (!aligned(Y, 16) || (T_save && !aligned(T_save, 4))) return QLORA_ERR_ALIGN;
+  const int64_t N = W->rows, K = W->cols;
+  const Layout L = plan(M, N, K, r);
+  if (ws_bytes < L.fwd_total) return QLORA_ERR_WORKSPACE;
+  try {
+    if (tables_status() != 0) return QLORA_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    char* base = static_cast<char*>(ws);
+    const int rp = (int)(cdiv(r, 32) * 32);
+    float* partT = reinterpret_cast<float*>(base + L.partT);
+    float* T32 = T_save ? T_save : reinterpret_cast<float*>(base + L.T32);
+    uint16_t* Ts = reinterpret_cast<uint16_t*>(base + L.Ts);
+    const uint16_t* Xh = static_cast<const uint16_t*>(X);
+    const uint16_t* Ah = static_cast<const uint16_t*>(A);
+    const uint16_t* Bh = static_cast<const uint16_t*>(B);
+
+    // T = X A^T, float32 [M, r]; Ts = bf16(scale * T) [M, rp]
+    QLORA_TRY(launch_proj(Xh, Ah, (int)M, (int)K, (int)r, rp, L.tsplit, partT, s));
+    QLORA_TRY(launch_finalize(partT, L.tsplit, (int)M, (int)r, rp, scale, T32, Ts, s));
+
+    if (M <= kGemvMaxM) {
+      float* gp = reinterpret_cast<float*>(base + L.gemvp);
+      QLORA_TRY(launch_gemv(Xh, W->codes, W->c2_fp8, W->c1, (int)N, (int)K, (int)M, L.gsplit, gp, s));
+      QLORA_TRY(launch_gemv_finalize(gp, L.gsplit, (int)M, (int)N, T32, Bh, (int)r, scale,
+                                     static_cast<uint16_t*>(Y), s));
+      return QLORA_OK;
+    }
+    const uint16_t* Br = Bh;
+    if (rp != r) {
+      uint16_t* Bpad = reinterpret_cast<uint16_t*>(base + L.Bpad);
+      QLORA_TRY(launch_relayout(Bh, N, r, r, false, Bpad, N, rp, rp, s));
+      Br = Bpad;
+    }
+    GemmParams p;
+    p.act = Xh;
+    p.codes = W->codes;
+    p.c2 = W->c2_fp8;
+    p.c1 = W->c1;
+    p.wN = N;
+    p.wK = K;
+    p.lora_l = Ts;
+    p.lora_r = Br;
+    p.rp = rp;
+    p.out = static_cast<uint16_t*>(Y);
+    p.M = (int)M;
+    p.Nout = (int)N;
+    p.Kred = (int)K;
+    p.lv = host_levels();
+    QLORA_TRY(launch_gemm(p, false, s));
+    return QLORA_OK;
+  } catch (...) {
+    return QLORA_ERR_DEVICE;
+  }
+}
+
+int qlora_linear_bwd(const qlora_nf4_weight* W, const void* X, const void* A, const void* B,
+                     const void* dY, const float* T_saved, int64_t M, int64_t r, float scale,
+                     void* dX, void* dA, void* dB, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_linear(W, X, A, B, M, r, scale, ws, ws_bytes);
+  if (st != QLORA_OK) return st;
+  if (!dY || !dA || !dB) return QLORA_ERR_NULL;
+  if (!aligned(dY, 16) || !aligned(dA, 16) || !aligned(dB, 16) || (dX && !aligned(dX, 16)) ||
+      (T_saved && !aligned(T_saved, 4)))
+    return QLORA_ERR_ALIGN;
+  const int64_t N = W->rows, K = W->cols;
+  const Layout L = plan(M, N, K, r);
+  if (ws_bytes < L.bwd_total) return QLORA_ERR_WORKSPACE;
+  try {
+    if (tables_status() != 0) return QLORA_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    char* base = static_cast<char*>(ws);
+    const int rp = (int)(cdiv(r, 32) * 32);
+    const uint16_t* Xh = static_cast<const uint16_t*>(X);
+    const uint16_t* Ah = static_cast<const uint16_t*>(A);
+    const uint16_t* Bh = static_cast<const uint16_t*>(B);
+    const uint16_t* dYh = static_cast<const uint16_t*>(dY);
+    uint16_t* Bt = reinterpret_cast<uint16_t*>(base + L.Bt);
+    uint16_t* At = reinterpret_cast<uint16_t*>(base + L.At);
+    float* partU = reinterpret_cast<float*>(base + L.partU);
+    float* U32 = reinterpret_cast<float*>(base + L.U32);
+    uint16_t* Us = reinterpret_cast<uint16_t*>(base + L.Us);
+    float* gpart = reinterpret_cast<float*>(base + L.gpart);
+
+    // T (float32 [M, r]): saved by the forward, or recomputed
+    const float* T = T_saved;
+    if (!T) {
+      float* partT = reinterpret_cast<float*>(base + L.partT);
+      float* T32 = reinterpret_cast<float*>(base + L.T32);
+      uint16_t* Ts = reinterpret_cast<uint16_t*>(base + L.Ts);
+      QLORA_TRY(launch_proj(Xh, Ah, (int)M, (int)K, (int)r, rp, L.tsplit, partT, s));
+      QLORA_TRY(launch_finalize(partT, L.tsplit, (int)M, (int)r, rp, 1.0f, T32, Ts, s));
+      T = T32;
+    }
+    // U = dY B: B^T [r, N] is the row operand of the projection
+    QLORA_TRY(launch_relayout(Bh, N, r, r, true, Bt, r, N, N, s));
+    QLORA_TRY(launch_proj(dYh, Bt, (int)M, (int)N, (int)r, rp, L.usplit, partU, s));
+    QLORA_TRY(launch_finalize(partU, L.usplit, (int)M, (int)r, rp, scale, U32, Us, s));
+
+    if (dX) {
+      // dX = dY W~ + (s U) A; A^T [K, rp] is the column operand of the epilogue
+      QLORA_TRY(launch_relayout(Ah, r, K, K, true, At, K, rp, rp, s));
+      GemmParams p;
+      p.act = dYh;
+      p.codes = W->codes;
+      p.c2 = W->c2_fp8;
+      p.c1 = W->c1;
+      p.wN = N;
+      p.wK = K;
+      p.lora_l = Us;
+      p.lora_r = At;
+      p.rp = rp;
+      p.out = static_cast<uint16_t*>(dX);
+      p.M = (int)M;
+      p.Nout = (int)K;
+      p.Kred = (int)N;
+      p.lv = host_levels();
+      QLORA_TRY(launch_gemm(p, true, s));
+    }
+    // dA = s U^T X  [r, K]
+    QLORA_TRY(launch_grad(U32, Xh, (int)M, (int)K, (int)r, rp, L.sA, gpart, s));
+    QLORA_TRY(launch_grad_reduce(gpart, L.sA, (int)r, rp, (int)K, scale, false, static_cast<uint16_t*>(dA), s));
+    // dB = s dY^T T  [N, r], computed as (T^T dY)^T
+    QLORA_TRY(launch_grad(T, dYh, (int)M, (int)N, (int)r, rp, L.sB, gpart, s));
+    QLORA_TRY(launch_grad_reduce(gpart, L.sB, (int)r, rp, (int)N, scale, true, static_cast<uint16_t*>(dB), s));
+    return QLORA_OK;
+  } catch (...) {
+    return QLORA_ERR_DEVICE;
+  }
+}
+
+}  // extern "C"

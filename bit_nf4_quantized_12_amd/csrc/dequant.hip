@@ -1,0 +1,96 @@
+// Dequantisation of the stored NF4 + double-quantised format.
+//
+// "QLoRA: Efficient Finetuning of Quantized LLMs" (inquiringlines.com),
+// "Method": whenever a stored weight is used it is dequantised to BFloat16.
+// Per weight: W^ = fp32(q[code] * c^_b) with c^_b = fp32(e4m3(c2_b) * c1_g);
+// the bf16 output is W~ = bf16(W^), round to nearest even.
+//
+// Each lane turns one 4-byte word of codes (8 weights, inside one block)
+// into 32 B (fp32) or 16 B (bf16) of output. The 16 levels sit in LDS, where
+// a lookup is conflict free (16 distinct dwords in 16 banks: equal codes
+// broadcast). Bandwidth kernel: 0.5 + 1/64 B read and 4 or 2 B written per
+// weight; four independent words per lane keep loads in flight.
+#include "launch.hpp"
+
+namespace qlora {
+namespace {
+
+template <bool BF16>
+__device__ __forceinline__ void emit8(void* __restrict__ out, int64_t e, uint32_t word, float chat,
+                                      const float* __restrict__ sq) {
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = __fmul_rn(sq[(word >> (4 * i)) & 15u], chat);
+  if (BF16) {
+    uint4 o = make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]),
+                         pack_bf16(f[6], f[7]));
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + e) = o;
+  } else {
+    float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + e);
+    p[0] = make_float4(f[0], f[1], f[2], f[3]);
+    p[1] = make_float4(f[4], f[5], f[6], f[7]);
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
+                                                       const uint8_t* __restrict__ c2,
+                                                       const float* __restrict__ c1, int64_t n,
+                                                       void* __restrict__ out, Levels lv) {
+  __shared__ float sq[16];
+  if (threadIdx.x < 16) sq[threadIdx.x] = lv.q[threadIdx.x];
+  __syncthreads();
+
+  const int64_t nwords = n >> 3;  // full 8-weight words
+  const uint32_t* cw = reinterpret_cast<const uint32_t*>(codes);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  // four words per lane per step, each a full grid stride apart (coalesced)
+  for (; i + 3 * stride < nwords; i += 4 * stride) {
+    uint32_t wd[4];
+    float cs[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) wd[u] = cw[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) cs[u] = block_scale(c2, c1, (i + u * stride) >> 3);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) emit8<BF16>(out, (i + u * stride) * 8, wd[u], cs[u], sq);
+  }
+  for (; i < nwords; i += stride) emit8<BF16>(out, i * 8, cw[i], block_scale(c2, c1, i >> 3), sq);
+
+  // short tail (n % 8 weights), one thread
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    for (int64_t e = nwords * 8; e < n; ++e) {
+      const uint32_t code = (codes[e >> 1] >> (4 * (e & 1))) & 15u;
+      const float v = __fmul_rn(sq[code], block_scale(c2, c1, e >> 6));
+      if (BF16) {
+        const __bf16 h = (__bf16)v;
+        reinterpret_cast<uint16_t*>(out)[e] = __builtin_bit_cast(uint16_t, h);
+      } else {
+        reinterpret_cast<float*>(out)[e] = v;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, int64_t n,
+                          bool bf16_out, void* out, hipStream_t s) {
+  const int64_t nwords = n >> 3;
+  int64_t blocks = (nwords + 255) / 256;
+  // a few resident waves per SIMD are enough for a streaming kernel;
+  // a grid-stride loop covers the rest
+  const int64_t cap = 256 * 16;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  if (bf16_out)
+    hipLaunchKernelGGL(dequant_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, codes, c2, c1,
+                       n, out, host_levels());
+  else
+    hipLaunchKernelGGL(dequant_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, codes, c2,
+                       c1, n, out, host_levels());
+  return hipGetLastError();
+}
+
+}  // namespace qlora

@@ -1,0 +1,43 @@
+// Host-side launchers of the library's kernels (one per .hip file).
+#pragma once
+
+#include "common.hpp"
+
+namespace qlora {
+
+struct GemmParams {
+  const uint16_t* act;     // [M, Kred] bf16, row pitch Kred
+  const uint8_t* codes;    // NF4 codes of W [wN, wK]
+  const uint8_t* c2;
+  const float* c1;
+  int64_t wN, wK;
+  const uint16_t* lora_l;  // [M, rp] bf16 (scale folded in), or null
+  const uint16_t* lora_r;  // [Nout, rp] bf16, or null
+  int rp;                  // multiple of 32
+  uint16_t* out;           // [M, Nout] bf16
+  int M, Nout, Kred;
+  Levels lv;
+};
+
+hipError_t launch_quantize(const void* w, int64_t n, uint8_t* codes, uint8_t* c2, float* c1,
+                           hipStream_t s);
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, int64_t n,
+                          bool bf16_out, void* out, hipStream_t s);
+hipError_t launch_gemm(const GemmParams& p, bool transposed_w, hipStream_t s);
+hipError_t launch_proj(const uint16_t* L, const uint16_t* R, int M, int Kr, int r, int rp,
+                       int nsplit, float* part, hipStream_t s);
+hipError_t launch_finalize(const float* part, int nsplit, int M, int r, int rp, float scale,
+                           float* P32, uint16_t* Ps, hipStream_t s);
+hipError_t launch_grad(const float* P, const uint16_t* Q, int M, int C, int r, int rp, int nsplit,
+                       float* part, hipStream_t s);
+hipError_t launch_grad_reduce(const float* part, int nsplit, int r, int rp, int C, float scale,
+                              bool transpose, uint16_t* out, hipStream_t s);
+hipError_t launch_relayout(const uint16_t* in, int64_t rows_in, int64_t cols_in, int64_t ldi,
+                           bool transpose, uint16_t* out, int64_t rows_out, int64_t cols_out,
+                           int64_t ldo, hipStream_t s);
+hipError_t launch_gemv(const uint16_t* X, const uint8_t* codes, const uint8_t* c2, const float* c1,
+                       int N, int K, int M, int nsplit, float* part, hipStream_t s);
+hipError_t launch_gemv_finalize(const float* part, int nsplit, int M, int N, const float* T,
+                                const uint16_t* B, int r, float scale, uint16_t* Y, hipStream_t s);
+
+}  // namespace qlora

@@ -1,0 +1,309 @@
+// The rank-r side of the LoRA linear layer.
+//
+// "QLoRA: Efficient Fine-Tuning of Quantized Language Models"
+// (mbrenndoerfer.com), section "Low-Rank Adaptation (LoRA)": the adapter
+// update is B A with A r x d and B d x r; "QLoRA: Efficient Finetuning of
+// Quantized LLMs" (inquiringlines.com), abstract: gradients are
+// backpropagated through the frozen 4-bit weight into the adapters.
+//
+// Kernels:
+//   proj     P = L R^T over a slice of the reduction (T = X A^T, U = dY B),
+//            float32 partial sums, no LDS traffic beyond a final reduction.
+//   finalize sums the slices: float32 P [M, r] and bf16(scale * P) padded to
+//            rp columns (the operand of the GEMM epilogue).
+//   grad     G = P^T Q over a slice of the M rows (dA = s U^T X,
+//            dB^T = s T^T dY): Q rows are transposed in registers with
+//            v_perm (no LDS), P is split into bf16 hi + lo so the float32
+//            intermediate keeps ~16 bits of precision in the MFMA.
+//   grad_reduce  sums the M slices in a fixed order (deterministic), scales
+//            and writes bf16 (optionally transposed).
+//   relayout small copies: transpose / zero-pad of A and B.
+#include "launch.hpp"
+
+namespace qlora {
+namespace {
+
+__device__ __forceinline__ uint4 load8_masked(const uint16_t* __restrict__ base, int64_t ld,
+                                              int64_t row, int64_t nrows, int64_t col,
+                                              int64_t ncols, bool vec) {
+  if (row >= nrows || col >= ncols) return make_uint4(0, 0, 0, 0);
+  const uint16_t* p = base + row * ld + col;
+  if (vec && col + 8 <= ncols) return *reinterpret_cast<const uint4*>(p);
+  uint32_t h[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = (col + i < ncols) ? p[i] : 0u;
+  return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+}
+
+// P[split][M][rp] = L[M, Kr] R[r, Kr]^T over reduction slice `split`.
+// KW = waves sharing one 16-row tile (each takes a quarter of the slice);
+// with KW = 1 every wave owns its own 16 rows.
+template <int KW>
+__global__ __launch_bounds__(256) void proj_kernel(const uint16_t* __restrict__ L,
+                                                    const uint16_t* __restrict__ R, int M, int Kr,
+                                                    int r, int rp, int kslice,
+                                                    float* __restrict__ part) {
+  __shared__ float red[(KW > 1) ? 4 * 16 * 256 : 1];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int rows_per_wg = 16 * (4 / KW);
+  const int m0 = blockIdx.x * rows_per_wg + 16 * (w / KW);
+  const int ks = blockIdx.y;
+  const int kbeg = ks * kslice;
+  const int kend = min(Kr, kbeg + kslice);
+  const int nt = rp >> 4;
+  const bool vec = (Kr & 7) == 0;
+
+  f32x4 acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int k = kbeg + 32 * (w % KW); k < kend; k += 32 * KW) {
+    const int col = k + 8 * (l >> 4);
+    const bf16x8 a = __builtin_bit_cast(bf16x8, load8_masked(L, Kr, m0 + (l & 15), M, col, kend, vec));
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j < nt) {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, load8_masked(R, Kr, 16 * j + (l & 15), r, col, kend, vec));
+        acc[j] = mfma16(a, b, acc[j]);
+      }
+    }
+  }
+
+  // D[i][j]: lane holds rows 4 (l >> 4) + v, column l & 15 of each 16 x 16 tile
+  if (KW == 1) {
+    float* dst = part + (int64_t)ks * M * rp;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j >= nt) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = m0 + 4 * (l >> 4) + v;
+        if (row < M) dst[(int64_t)row * rp + 16 * j + (l & 15)] = acc[j][v];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j >= nt) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[(w * 16 + 4 * (l >> 4) + v) * 256 + 16 * j + (l & 15)] = acc[j][v];
+    }
+    __syncthreads();
+    float* dst = part + (int64_t)ks * M * rp;
+    for (int idx = tid; idx < 16 * rp; idx += 256) {
+      const int i = idx / rp, j = idx % rp;
+      const float s = red[(0 * 16 + i) * 256 + j] + red[(1 * 16 + i) * 256 + j] +
+                      red[(2 * 16 + i) * 256 + j] + red[(3 * 16 + i) * 256 + j];
+      const int row = m0 + i;
+      if (row < M) dst[(int64_t)row * rp + j] = s;
+    }
+  }
+}
+
+// Sum the reduction slices: P32 [M, r] float32 (may be null) and
+// Ps [M, rp] = bf16(scale * P), zero in columns r .. rp-1.
+__global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ part, int nsplit,
+                                                        int M, int r, int rp, float scale,
+                                                        float* __restrict__ P32,
+                                                        uint16_t* __restrict__ Ps) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)M * rp) return;
+  const int64_t m = idx / rp;
+  const int j = (int)(idx % rp);
+  float v = 0.0f;
+  for (int s = 0; s < nsplit; ++s) v += part[(int64_t)s * M * rp + idx];
+  if (j < r) {
+    if (P32) P32[m * r + j] = v;
+    const __bf16 h = (__bf16)(scale * v);
+    Ps[idx] = __builtin_bit_cast(uint16_t, h);
+  } else {
+    Ps[idx] = 0;
+  }
+}
+
+// part[s][j][c] = sum over rows m of slice s of P[m][j] * Q[m][c],
+// j in [64 jc, 64 jc + 64), c in [128 cg, 128 cg + 128).
+__global__ __launch_bounds__(256) void grad_kernel(const float* __restrict__ P,
+                                                    const uint16_t* __restrict__ Q, int M, int C,
+                                                    int r, int rp, int mchunk,
+                                                    float* __restrict__ part) {
+  __shared__ float red[2 * 64 * 129];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int cg = blockIdx.x, s = blockIdx.y, jc = blockIdx.z;
+  const int mbeg = s * mchunk;
+  const int mend = min(M, mbeg + mchunk);
+  const int c0 = cg * 128 + 8 * (l & 15);
+  const int g = l >> 4;
+  const bool vec = (C & 7) == 0;
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int m = mbeg + 32 * w; m < mend; m += 128) {
+    uint4 rq[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rq[i] = load8_masked(Q, C, m + 8 * g + i, mend, c0, C, vec);
+    // B operand for column c0 + cc: Q[m + 8g + i][c0 + cc], i = 0..7
+    bf16x8 bq[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t lo[4], hi[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t x0 = (&rq[2 * i].x)[e], x1 = (&rq[2 * i + 1].x)[e];
+        lo[i] = __builtin_amdgcn_perm(x1, x0, 0x05040100u);  // element 2e of rows 2i, 2i+1
+        hi[i] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);  // element 2e+1
+      }
+      bq[2 * e] = __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+      bq[2 * e + 1] = __builtin_bit_cast(bf16x8, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+    }
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      const int j = jc * 64 + 16 * jt + (l & 15);
+      float pv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = m + 8 * g + i;
+        pv[i] = (j < r && row < mend) ? P[(int64_t)row * r + j] : 0.0f;
+      }
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const __bf16 h0 = (__bf16)pv[2 * i], h1 = (__bf16)pv[2 * i + 1];
+        const float r0 = pv[2 * i] - (float)h0, r1 = pv[2 * i + 1] - (float)h1;
+        hw[i] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        lw[i] = pack_bf16(r0, r1);
+      }
+      const bf16x8 ah = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      const bf16x8 al = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) {
+        acc[jt][cc] = mfma16(ah, bq[cc], acc[jt][cc]);
+        acc[jt][cc] = mfma16(al, bq[cc], acc[jt][cc]);
+      }
+    }
+  }
+
+  // reduce the four waves: 3,2 -> LDS, 0,1 add; 1 -> LDS, 0 adds
+  auto put = [&](int slot) {
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[slot * 64 * 129 + l * 129 + jt * 32 + cc * 4 + v] = acc[jt][cc][v];
+  };
+  auto add = [&](int slot) {
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[jt][cc][v] += red[slot * 64 * 129 + l * 129 + jt * 32 + cc * 4 + v];
+  };
+  if (w >= 2) put(w - 2);
+  __syncthreads();
+  if (w < 2) add(w);
+  __syncthreads();
+  if (w == 1) put(0);
+  __syncthreads();
+  if (w == 0) {
+    add(0);
+    float* dst = part + (int64_t)s * rp * C;
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = jc * 64 + 16 * jt + 4 * (l >> 4) + v;
+        if (j >= rp) continue;
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) {
+          const int c = c0 + cc;
+          if (c < C) dst[(int64_t)j * C + c] = acc[jt][cc][v];
+        }
+      }
+  }
+}
+
+// out = bf16(scale * sum_s part[s][j][c]); j < r, c < C. Transposed: out[c][j].
+__global__ __launch_bounds__(256) void grad_reduce_kernel(const float* __restrict__ part,
+                                                           int nsplit, int r, int rp, int C,
+                                                           float scale, bool transpose,
+                                                           uint16_t* __restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)r * C) return;
+  int64_t j, c;
+  if (transpose) { c = idx / r; j = idx % r; } else { j = idx / C; c = idx % C; }
+  float v = 0.0f;
+  for (int s = 0; s < nsplit; ++s) v += part[(int64_t)s * rp * C + j * C + c];
+  const __bf16 h = (__bf16)(scale * v);
+  out[idx] = __builtin_bit_cast(uint16_t, h);
+}
+
+// out[i][j] (pitch ldo, i < rows_out, j < cols_out) = in[j][i] if transpose
+// else in[i][j], zero outside the input [rows_in, cols_in] (pitch ldi).
+__global__ __launch_bounds__(256) void relayout_kernel(const uint16_t* __restrict__ in,
+                                                        int64_t rows_in, int64_t cols_in,
+                                                        int64_t ldi, bool transpose,
+                                                        uint16_t* __restrict__ out,
+                                                        int64_t rows_out, int64_t cols_out,
+                                                        int64_t ldo) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows_out * cols_out) return;
+  const int64_t i = idx / cols_out, j = idx % cols_out;
+  const int64_t si = transpose ? j : i, sj = transpose ? i : j;
+  out[i * ldo + j] = (si < rows_in && sj < cols_in) ? in[si * ldi + sj] : (uint16_t)0;
+}
+
+}  // namespace
+
+hipError_t launch_proj(const uint16_t* L, const uint16_t* R, int M, int Kr, int r, int rp,
+                       int nsplit, float* part, hipStream_t s) {
+  const int kslice = ((Kr + nsplit - 1) / nsplit + 31) / 32 * 32;
+  if (M <= 16) {
+    dim3 grid(1, nsplit);
+    hipLaunchKernelGGL(proj_kernel<4>, grid, dim3(256), 0, s, L, R, M, Kr, r, rp, kslice, part);
+  } else {
+    dim3 grid((M + 63) / 64, nsplit);
+    hipLaunchKernelGGL(proj_kernel<1>, grid, dim3(256), 0, s, L, R, M, Kr, r, rp, kslice, part);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const float* part, int nsplit, int M, int r, int rp, float scale,
+                           float* P32, uint16_t* Ps, hipStream_t s) {
+  const int64_t total = (int64_t)M * rp;
+  hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part,
+                     nsplit, M, r, rp, scale, P32, Ps);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad(const float* P, const uint16_t* Q, int M, int C, int r, int rp, int nsplit,
+                       float* part, hipStream_t s) {
+  const int mchunk = ((M + nsplit - 1) / nsplit + 31) / 32 * 32;
+  dim3 grid((C + 127) / 128, nsplit, (rp + 63) / 64);
+  hipLaunchKernelGGL(grad_kernel, grid, dim3(256), 0, s, P, Q, M, C, r, rp, mchunk, part);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_reduce(const float* part, int nsplit, int r, int rp, int C, float scale,
+                              bool transpose, uint16_t* out, hipStream_t s) {
+  const int64_t total = (int64_t)r * C;
+  hipLaunchKernelGGL(grad_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                     part, nsplit, r, rp, C, scale, transpose, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_relayout(const uint16_t* in, int64_t rows_in, int64_t cols_in, int64_t ldi,
+                           bool transpose, uint16_t* out, int64_t rows_out, int64_t cols_out,
+                           int64_t ldo, hipStream_t s) {
+  const int64_t total = rows_out * cols_out;
+  hipLaunchKernelGGL(relayout_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, in,
+                     rows_in, cols_in, ldi, transpose, out, rows_out, cols_out, ldo);
+  return hipGetLastError();
+}
+
+}  // namespace qlora

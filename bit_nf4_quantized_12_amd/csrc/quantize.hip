@@ -1,0 +1,166 @@
+// NF4 quantiser with double quantisation of the block constants.
+//
+// "QLoRA: Efficient Finetuning of Quantized LLMs" (inquiringlines.com),
+// "Method": step (3) of "4-bit NormalFloat Quantization" (normalise each
+// block of 64 into [-1, 1] by its absolute maximum, then take the nearest
+// level) and "Double Quantization" (quantise the block constants again).
+//
+// One workgroup (4 wave64) per group of 256 blocks = 16384 weights = 32 KB
+// of bf16. Loads are 16 B per lane and fully coalesced; the block absmax is
+// a max over the 8 lanes that hold a block (DPP, no LDS); the group max is a
+// wave reduction plus 4 LDS slots. HBM traffic is the algorithmic minimum:
+// 2 B read and 0.5 + 1/64 + 4/16384 B written per weight.
+#include "launch.hpp"
+
+namespace qlora {
+namespace {
+
+__device__ __forceinline__ float dpp_max8(float v) {
+  // lanes of one block: 8 consecutive lanes. xor 1, xor 2 inside a quad,
+  // then the mirror inside 8 lanes pairs the two quads.
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// x = RN32(w / c) for one block. r = RN32(1 / c). With r correctly rounded,
+// q0 = RN(w r), e = w - c q0 (exact through the fused multiply-add) and
+// RN(q0 + e r) is the correctly rounded quotient (Markstein's theorem) as
+// long as nothing under- or overflows, which `fast` guarantees; otherwise
+// the IEEE division is used.
+__device__ __forceinline__ float div_block(float w, float c, float r, bool fast) {
+  if (fast) {
+    const float q0 = w * r;
+    const float e = __builtin_fmaf(-c, q0, w);
+    return __builtin_fmaf(e, r, q0);
+  }
+  return w / c;
+}
+
+__device__ __forceinline__ uint32_t nearest_code(float x, const float2* __restrict__ tab) {
+  int cell = (int)__builtin_fmaf(x, 16.0f, 16.0f);
+  cell = cell > 31 ? 31 : cell;
+  const float2 t = tab[cell];
+  return (uint32_t)__float_as_int(t.y) + (x > t.x ? 1u : 0u);
+}
+
+// E4M3 (OCP, bias 7) code of rho in [0, 1], round to nearest even.
+__device__ __forceinline__ uint32_t e4m3_code(float rho) {
+  if (rho >= 0x1p-6f) {
+    const uint32_t b = __float_as_uint(rho);
+    uint32_t kept = b >> 20;
+    const uint32_t rem = b & 0xFFFFFu;
+    kept += (rem > 0x80000u || (rem == 0x80000u && (kept & 1u))) ? 1u : 0u;
+    return kept - ((127u - 7u) << 3);
+  }
+  return (uint32_t)__builtin_rintf(rho * 512.0f);  // subnormal: m * 2^-9, m in 0..8
+}
+
+__global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ w, int64_t n,
+                                                        uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ c2,
+                                                        float* __restrict__ c1, QuantTable qt) {
+  __shared__ float2 s_tab[32];
+  __shared__ float s_wmax[4];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  if (tid < 32) s_tab[tid] = make_float2(qt.thr[tid], __int_as_float(qt.base[tid]));
+  __syncthreads();
+
+  const int64_t gbase = (int64_t)blockIdx.x * kGroup;
+  const int64_t nb = (n + kBlock - 1) / kBlock;
+  const bool full = gbase + kGroup <= n;
+
+  uint4 v[8];
+  if (full) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t e = gbase + wave * 4096 + j * 512 + lane * 8;
+      v[j] = *reinterpret_cast<const uint4*>(w + e);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t e = gbase + wave * 4096 + j * 512 + lane * 8;
+      uint32_t h[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[i] = (e + i < n) ? w[e + i] : 0u;
+      v[j] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+    }
+  }
+
+  float bmax[8];
+  float gmax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t e = gbase + wave * 4096 + j * 512 + lane * 8;
+    float f[8];
+    f[0] = bf16lo(v[j].x); f[1] = bf16hi(v[j].x);
+    f[2] = bf16lo(v[j].y); f[3] = bf16hi(v[j].y);
+    f[4] = bf16lo(v[j].z); f[5] = bf16hi(v[j].z);
+    f[6] = bf16lo(v[j].w); f[7] = bf16hi(v[j].w);
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+    m = dpp_max8(m);
+    bmax[j] = m;
+    gmax = fmaxf(gmax, m);
+
+    uint32_t word = 0x77777777u;  // an all-zero block maps to the exact zero
+    if (m > 0.0f) {
+      const bool fast = m >= 0x1p-100f && m <= 0x1p100f;
+      const float r = 1.0f / m;
+      word = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = div_block(f[i], m, r, fast);
+        word |= nearest_code(x, s_tab) << (4 * i);
+      }
+    }
+    if (full || e + 8 <= n) {
+      *reinterpret_cast<uint32_t*>(codes + (e >> 1)) = word;
+    } else if (e < n) {
+      // short tail: elements past n get code 0, bytes past ceil(n/2) are not written
+      const int valid = (int)(n - e);
+      const uint32_t keep = valid >= 8 ? 0xFFFFFFFFu : ((1u << (4 * valid)) - 1u);
+      word &= keep;
+      const int bytes = (valid + 1) >> 1;
+      for (int b = 0; b < bytes; ++b) codes[(e >> 1) + b] = (uint8_t)(word >> (8 * b));
+    }
+  }
+
+  gmax = wave_max(gmax);
+  if (lane == 0) s_wmax[wave] = gmax;
+  __syncthreads();
+  const float g = fmaxf(fmaxf(s_wmax[0], s_wmax[1]), fmaxf(s_wmax[2], s_wmax[3]));
+  if (tid == 0) c1[blockIdx.x] = g;
+  if ((lane & 7) == 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t b = (gbase >> 6) + wave * 64 + j * 8 + (lane >> 3);
+      if (b < nb) {
+        uint32_t code = 0;
+        if (g > 0.0f) code = e4m3_code(bmax[j] / g);
+        c2[b] = (uint8_t)code;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* w, int64_t n, uint8_t* codes, uint8_t* c2, float* c1,
+                           hipStream_t s) {
+  const int64_t groups = (n + kGroup - 1) / kGroup;
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)groups), dim3(256), 0, s,
+                     reinterpret_cast<const uint16_t*>(w), n, codes, c2, c1, host_quant_table());
+  return hipGetLastError();
+}
+
+}  // namespace qlora

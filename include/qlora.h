@@ -1,0 +1,148 @@
+/*
+ * qlora.h -- C ABI of the NF4 + double-quantisation + LoRA linear library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method is QLoRA as described on these pages:
+ *   [P2] "QLoRA: Efficient Finetuning of Quantized LLMs" (inquiringlines.com
+ *        paper text), section "Method", paragraphs "4-bit NormalFloat
+ *        Quantization" and "Double Quantization"; the abstract.
+ *   [P1] "QLoRA: Efficient Fine-Tuning of Quantized Language Models"
+ *        (mbrenndoerfer.com), section "Low-Rank Adaptation (LoRA)".
+ *   [P3] "Efficient Language Model Fine-Tuning with QLoRA on
+ *        Resource-Constrained Hardware" (marciocunha.net), the LoraConfig
+ *        example (r, lora_alpha).
+ *
+ * Conventions shared by every call:
+ *  - Pointers marked "device" are HIP device pointers; the library never
+ *    allocates, frees or retains memory and keeps no pointer after return.
+ *    Outputs are overwritten, never accumulated into.
+ *  - Device work is enqueued asynchronously on `stream` (a hipStream_t;
+ *    NULL means the default stream). A return of QLORA_OK means the work was
+ *    enqueued; faults inside kernels surface at the caller's next
+ *    synchronisation.
+ *  - Arguments are validated before any HIP call. On any error nothing is
+ *    launched and no output is touched. No C++ exception crosses the ABI.
+ *  - Weights W are [N, K] row-major (out x in), flattened in C order for the
+ *    blockwise format below. Activations are rows of tokens: X [M, K],
+ *    Y [M, N]. LoRA adapters: A [r, K], B [N, r]. All bf16 row-major,
+ *    contiguous. The layer is Y = X W~^T + s (X A^T) B^T.
+ *  - Stored NF4 + DQ format of n weights (blocks of 64 weights, groups of
+ *    256 blocks):
+ *      codes  uint8[ceil(n/2)]   4-bit level indices, element 2i in the low
+ *                                nibble of byte i (pad nibble 0 when n odd)
+ *      c2     uint8[ceil(n/64)]  OCP FP8 E4M3 code of absmax_b / c1_g
+ *      c1     float[ceil(ceil(n/64)/256)]  per-group max of absmax_b
+ *    Dequantised weight: W^_i = fp32( q[code_i] * fp32( e4m3(c2_b) * c1_g ) );
+ *    the matmul operand is W~ = bf16(W^) (round to nearest even).
+ *
+ * Thread safety: every call may be made concurrently from several host
+ * threads; the only global state is an immutable table built once.
+ */
+#ifndef QLORA_H
+#define QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_ERR_NULL = 1,        /* a required pointer is NULL                 */
+  QLORA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent     */
+  QLORA_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned           */
+  QLORA_ERR_UNSUPPORTED = 4, /* a valid but unsupported mode or value      */
+  QLORA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than needed   */
+  QLORA_ERR_DEVICE = 6       /* a HIP call failed (launch or device query) */
+} qlora_status;
+
+typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
+
+/* A quantised weight [rows=N, cols=K]: views into caller-owned device
+ * memory holding the stored format above for n = rows * cols. */
+typedef struct {
+  const uint8_t* codes;
+  const uint8_t* c2_fp8;
+  const float* c1;
+  int64_t rows; /* N, out features */
+  int64_t cols; /* K, in features  */
+} qlora_nf4_weight;
+
+/* The 16 NF4 levels in ascending order, as float32 (code 0 = -1, code 7 = 0,
+ * code 15 = +1). [P2] "4-bit NormalFloat Quantization": quantiles of N(0,1)
+ * -- 9 on the positive side and 8 on the negative side, one of the two zeros
+ * dropped -- normalised into [-1, 1]. The outermost quantile is taken at
+ * probability 1 - (1/32 + 1/30)/2, a reading (the pages omit the value).
+ * `out`: host memory, 16 floats. Synchronous, no GPU use.
+ * Errors: QLORA_ERR_NULL if out is NULL. */
+int qlora_nf4_levels(float out[16]);
+
+/* Quantise n bf16 weights to NF4 with double quantisation.
+ * [P2] "4-bit NormalFloat Quantization" step (3): each block of 64 is
+ * divided by its absolute maximum (IEEE float32 division) and mapped to the
+ * nearest level (a tie goes to the lower code; an all-zero block to code 7).
+ * [P2] "Double Quantization": the block absmaxes are quantised again, to
+ * FP8 E4M3 (round to nearest even) relative to the max of their group of
+ * 256; a group whose max is 0 stores c1 = 0 and c2 = 0.
+ * w_bf16: device, n bf16 (16-byte aligned). codes / c2_fp8 / c1: device
+ * outputs sized as in the stored format (codes and c2 16-byte aligned,
+ * c1 4-byte aligned). Weights must be finite (non-finite input gives
+ * unspecified codes). Errors: NULL, SHAPE (n < 1), ALIGN, DEVICE. */
+int qlora_quantize_nf4_dq(const void* w_bf16, int64_t n, uint8_t* codes,
+                          uint8_t* c2_fp8, float* c1, void* stream);
+
+/* Dequantise n weights of the stored format: [P2] "Method": a stored weight
+ * is dequantised to BFloat16 whenever it is used. out_dtype QLORA_F32 writes
+ * W^ (float32, bit-exact per the formula above); QLORA_BF16 writes W~.
+ * codes / c2_fp8 / c1: device inputs; out: device output of n elements,
+ * 16-byte aligned. Errors: NULL, SHAPE (n < 1), ALIGN, UNSUPPORTED (dtype),
+ * DEVICE. */
+int qlora_dequant(const uint8_t* codes, const uint8_t* c2_fp8, const float* c1,
+                  int64_t n, int out_dtype, void* out, void* stream);
+
+/* Workspace bytes needed by qlora_linear_fwd and qlora_linear_bwd for these
+ * sizes (the larger of the two; 0 on invalid sizes). */
+size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
+
+/* LoRA linear forward on the frozen quantised weight:
+ *   T = X A^T (float32 [M, r]);  Y = X W~^T + scale * T B^T  (bf16 [M, N]).
+ * [P1] "Low-Rank Adaptation (LoRA)": x_out = (W_q + B A) x_in with B d x r
+ * and A r x d; [P2] "Method": W~ is the bf16 dequantised weight and the
+ * product runs in 16-bit with float32 accumulation. scale = lora_alpha / r
+ * ([P3] LoraConfig; a reading, the pages show no formula).
+ * W: host struct of device views (rows N, cols K; K % 64 == 0).
+ * X [M, K], A [r, K], B [N, r]: device bf16. Y [M, N]: device bf16 output.
+ * T_save: device float32 [M, r] output, or NULL. ws: device workspace of at
+ * least qlora_linear_workspace_bytes(M, N, K, r) bytes, 256-byte aligned.
+ * Limits: 1 <= M, 1 <= N, 64 <= K, K % 64 == 0, 1 <= r <= 256, scale finite,
+ * M * max(N, K) < 2^31. Errors: NULL, SHAPE, ALIGN, UNSUPPORTED,
+ * WORKSPACE, DEVICE. */
+int qlora_linear_fwd(const qlora_nf4_weight* W, const void* X, const void* A,
+                     const void* B, int64_t M, int64_t r, float scale, void* Y,
+                     float* T_save, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of qlora_linear_fwd for the upstream gradient dY [M, N] (bf16).
+ * [P2] abstract: gradients flow through the frozen 4-bit weight into the
+ * adapters only, so there is no weight gradient:
+ *   U  = dY B                      (float32, internal)
+ *   dX = dY W~ + scale * U A       (bf16 [M, K]; skipped when dX is NULL)
+ *   dA = scale * U^T X             (bf16 [r, K])
+ *   dB = scale * dY^T T            (bf16 [N, r]), T = X A^T
+ * T_saved: the T_save of the forward (float32 [M, r]) or NULL to recompute.
+ * Other arguments and limits as for qlora_linear_fwd. dA/dB are reduced in a
+ * fixed order: results are bit-identical from run to run. */
+int qlora_linear_bwd(const qlora_nf4_weight* W, const void* X, const void* A,
+                     const void* B, const void* dY, const float* T_saved,
+                     int64_t M, int64_t r, float scale, void* dX, void* dA,
+                     void* dB, void* ws, size_t ws_bytes, void* stream);
+
+/* Static text for a status code ("unknown status" for other values). */
+const char* qlora_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_H */

@@ -1,0 +1,138 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, computes the NF4 level table on the host bit-exactly like the
+oracle, and rejects bad arguments with the documented status before any HIP
+call (fake device addresses are never dereferenced on these paths)."""
+
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_nf4_quantized_12_amd as q
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora.h")
+
+OK, NULL, SHAPE, ALIGN, UNSUPPORTED, WORKSPACE, DEVICE = range(7)
+FAKE = 0x10000  # an aligned address that is never touched by validation failures
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return q.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text))
+    assert {"qlora_nf4_levels", "qlora_quantize_nf4_dq", "qlora_dequant", "qlora_linear_fwd",
+            "qlora_linear_bwd"} <= declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_levels_bit_exact_with_oracle():
+    got = q.qlora_nf4_levels().numpy()
+    np.testing.assert_array_equal(got.view(np.uint32), oracle.nf4_levels().view(np.uint32))
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert lib.qlora_status_string(s)
+    assert lib.qlora_status_string(99) == b"unknown status"
+
+
+def test_levels_null(lib):
+    assert lib.qlora_nf4_levels(None) == NULL
+
+
+def test_quantize_validation(lib):
+    f = lib.qlora_quantize_nf4_dq
+    assert f(None, 64, FAKE, FAKE, FAKE, None) == NULL
+    assert f(FAKE, 64, None, FAKE, FAKE, None) == NULL
+    assert f(FAKE, 0, FAKE, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, -5, FAKE, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE + 2, 64, FAKE, FAKE, FAKE, None) == ALIGN
+    assert f(FAKE, 64, FAKE + 8, FAKE, FAKE, None) == ALIGN
+    assert f(FAKE, 64, FAKE, FAKE, FAKE + 1, None) == ALIGN
+
+
+def test_dequant_validation(lib):
+    f = lib.qlora_dequant
+    assert f(None, FAKE, FAKE, 64, 0, FAKE, None) == NULL
+    assert f(FAKE, FAKE, FAKE, 0, 0, FAKE, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, 64, 7, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, 64, 0, FAKE + 4, None) == ALIGN
+
+
+def _w(rows, cols, codes=FAKE, c2=FAKE, c1=FAKE):
+    return q._Weight(codes, c2, c1, rows, cols)
+
+
+def test_workspace_bytes(lib):
+    assert lib.qlora_linear_workspace_bytes(0, 10, 64, 8) == 0
+    assert lib.qlora_linear_workspace_bytes(4, 10, 65, 8) == 0
+    assert lib.qlora_linear_workspace_bytes(4, 10, 64, 0) == 0
+    assert lib.qlora_linear_workspace_bytes(4, 10, 64, 257) == 0
+    for M in (1, 16, 17, 8192):
+        assert lib.qlora_linear_workspace_bytes(M, 4096, 4096, 64) > 0
+
+
+def test_linear_fwd_validation(lib):
+    f = lib.qlora_linear_fwd
+    big = 1 << 40
+    w = _w(128, 128)
+    args = lambda **k: dict(dict(W=ctypes.byref(w), X=FAKE, A=FAKE, B=FAKE, M=4, r=8, s=1.0, Y=FAKE,  # noqa: E731
+                                 T=None, ws=FAKE * 16, wsb=big, st=None), **k)
+    call = lambda a: f(a["W"], a["X"], a["A"], a["B"], a["M"], a["r"], a["s"], a["Y"], a["T"],  # noqa: E731
+                       a["ws"], a["wsb"], a["st"])
+    assert call(args(W=None)) == NULL
+    assert call(args(X=None)) == NULL
+    assert call(args(Y=None)) == NULL
+    assert call(args(ws=None)) == WORKSPACE
+    assert call(args(M=0)) == SHAPE
+    assert call(args(r=0)) == SHAPE
+    assert call(args(r=300)) == SHAPE
+    assert call(args(s=math.nan)) == UNSUPPORTED
+    assert call(args(s=math.inf)) == UNSUPPORTED
+    assert call(args(X=FAKE + 2)) == ALIGN
+    assert call(args(ws=FAKE * 16 + 16)) == ALIGN
+    assert call(args(T=FAKE + 2)) == ALIGN
+    assert call(args(wsb=100)) == WORKSPACE
+    w2 = _w(128, 100)
+    assert call(args(W=ctypes.byref(w2))) == SHAPE   # K % 64 != 0
+    w3 = _w(128, 128, codes=None)
+    assert call(args(W=ctypes.byref(w3))) == NULL
+    w4 = _w(128, 128, codes=FAKE + 1)
+    assert call(args(W=ctypes.byref(w4))) == ALIGN
+
+
+def test_linear_bwd_validation(lib):
+    f = lib.qlora_linear_bwd
+    w = _w(128, 128)
+    big = 1 << 40
+
+    def call(**k):
+        a = dict(W=ctypes.byref(w), X=FAKE, A=FAKE, B=FAKE, dY=FAKE, T=None, M=4, r=8, s=1.0,
+                 dX=FAKE, dA=FAKE, dB=FAKE, ws=FAKE * 16, wsb=big)
+        a.update(k)
+        return f(a["W"], a["X"], a["A"], a["B"], a["dY"], a["T"], a["M"], a["r"], a["s"], a["dX"],
+                 a["dA"], a["dB"], a["ws"], a["wsb"], None)
+
+    assert call(dY=None) == NULL
+    assert call(dA=None) == NULL
+    assert call(dB=None) == NULL
+    assert call(dX=FAKE + 2) == ALIGN
+    assert call(M=-1) == SHAPE
+    assert call(s=math.nan) == UNSUPPORTED
+    assert call(wsb=10) == WORKSPACE
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        q.qlora_quantize_nf4_dq(torch.zeros(64, dtype=torch.bfloat16))

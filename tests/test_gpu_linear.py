@@ -1,0 +1,118 @@
+"""GPU parity of the LoRA linear forward and backward against the float64 oracle.
+
+The oracle quantises the same bf16 weight itself (its own codes), dequantises
+to W~ = bf16(W^) and evaluates the layer in float64. Outputs must be within
+rel-L2 4e-3 and max-abs 2e-2 x RMS (tests/parity.py). Large shapes compare
+sampled rows of Y and dX (each an independent set of dot products) and the
+full dA, dB.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_nf4_quantized_12_amd as q
+import oracle
+from bit_nf4_quantized_12_amd import synth
+from tests.parity import assert_close, bf16_bits_to_f32, report
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _oracle_weight(w32):
+    pk, c2, c1 = oracle.quantize_nf4_dq(w32)
+    return oracle.bf16_round(oracle.dequant(pk, c2, c1, w32.size)).reshape(w32.shape)
+
+
+def run_case(M, N, K, r, alpha, seed=0, cfg=100, rows=None, w_dist="normal", backward=True,
+             save_T=True):
+    report(f"linear parity: M={M} N={N} K={K} r={r} alpha={alpha} save_T={save_T}")
+    case = synth.linear_case(M, N, K, r, seed=seed, cfg=cfg, w_dist=w_dist)
+    s = alpha / r
+    Wt, Xt, At, Bt, dYt = (case[k][0].to(DEV) for k in ("W", "X", "A", "B", "dY"))
+    w32, x, a, b, dy = (case[k][1] for k in ("W", "X", "A", "B", "dY"))
+    W = q.quantize_weight(Wt)
+    Y, T = q.qlora_linear_fwd(W, Xt, At, Bt, s, save_T=save_T)
+    out = {"Y": Y}
+    if backward:
+        dX, dA, dB = q.qlora_linear_bwd(W, Xt, At, Bt, dYt, T, s)
+        out.update(dX=dX, dA=dA, dB=dB)
+    torch.cuda.synchronize()
+    got = {k: bf16_bits_to_f32(v) for k, v in out.items()}
+    if T is not None:
+        got["T"] = T.cpu().numpy()
+
+    Wo = _oracle_weight(w32)
+    sel = np.arange(M) if rows is None else np.asarray(rows)
+    Yr, Tr = oracle.linear_fwd(x[sel], Wo, a, b, s)
+    assert_close(got["Y"][sel], Yr, "Y")
+    if T is not None:
+        assert_close(got["T"][sel], Tr, "T")
+    if backward:
+        dXr, _, _ = oracle.linear_bwd(x[sel], Wo, a, b, dy[sel], s)
+        assert_close(got["dX"][sel], dXr, "dX")
+        _, dAr, dBr = oracle.linear_bwd(x, Wo, a, b, dy, s)
+        assert_close(got["dA"], dAr, "dA")
+        assert_close(got["dB"], dBr, "dB")
+    return got
+
+
+def test_single_linear_256_r8():
+    # 256 x 256 weight, 16 tokens, r = 8, alpha = 16 -> s = 2
+    run_case(16, 256, 256, 8, 16.0, cfg=1)
+
+
+@pytest.mark.parametrize("M,N,K,r", [
+    (1, 100, 64, 1), (3, 257, 192, 5), (16, 300, 320, 8), (17, 129, 128, 16),
+    (130, 200, 384, 33), (256, 512, 512, 64), (70, 1000, 640, 64), (129, 131, 64, 256),
+    (200, 96, 1024, 2),
+])
+def test_ragged_shapes(M, N, K, r):
+    run_case(M, N, K, r, 16.0, cfg=101)
+
+
+def test_recompute_T_matches_saved_T():
+    got_saved = run_case(40, 200, 256, 16, 16.0, cfg=102, save_T=True)
+    got_none = run_case(40, 200, 256, 16, 16.0, cfg=102, save_T=False)
+    for k in ("Y", "dX", "dA", "dB"):
+        np.testing.assert_array_equal(got_saved[k], got_none[k])
+
+
+def test_gemv_agrees_with_gemm_path():
+    # M = 16 runs the few-token kernel, M = 17 the tiled GEMM; row 0..15 agree
+    case = synth.linear_case(17, 700, 512, 64, cfg=103)
+    Wt, Xt, At, Bt = (case[k][0].to(DEV) for k in ("W", "X", "A", "B"))
+    W = q.quantize_weight(Wt)
+    Y16, _ = q.qlora_linear_fwd(W, Xt[:16].contiguous(), At, Bt, 0.25)
+    Y17, _ = q.qlora_linear_fwd(W, Xt, At, Bt, 0.25)
+    torch.cuda.synchronize()
+    a = bf16_bits_to_f32(Y16)
+    b = bf16_bits_to_f32(Y17)[:16]
+    assert np.max(np.abs(a - b)) <= 2e-2 * np.sqrt(np.mean(b * b))
+
+
+def test_backward_is_deterministic():
+    case = synth.linear_case(300, 520, 256, 64, cfg=104)
+    Wt, Xt, At, Bt, dYt = (case[k][0].to(DEV) for k in ("W", "X", "A", "B", "dY"))
+    W = q.quantize_weight(Wt)
+    _, T = q.qlora_linear_fwd(W, Xt, At, Bt, 0.25)
+    r1 = q.qlora_linear_bwd(W, Xt, At, Bt, dYt, T, 0.25)
+    r2 = q.qlora_linear_bwd(W, Xt, At, Bt, dYt, T, 0.25)
+    torch.cuda.synchronize()
+    for x, y in zip(r1, r2):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("M", [1, 16, 512])
+@pytest.mark.parametrize("N", [4096, 11008])
+def test_llama7b_projections_forward(M, N):
+    # few-token and small-GEMM regime: forward only
+    rows = None if M <= 16 else np.random.default_rng(M).choice(M, 128, replace=False)
+    run_case(M, N, 4096, 64, 16.0, cfg=2, rows=rows, backward=False)
+
+
+@pytest.mark.parametrize("N,K", [(4096, 4096), (11008, 4096), (4096, 11008)])
+def test_llama7b_layer_linears_8192_tokens(N, K):
+    rows = np.random.default_rng(N + K).choice(8192, 96, replace=False)
+    run_case(8192, N, K, 64, 16.0, cfg=3, rows=rows)
