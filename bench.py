@@ -1,0 +1,328 @@
+#!/usr/bin/env python3
+"""Throughput of the NF4 + double-quantisation + LoRA linear path on one MI355X.
+
+Step (the timed unit): forward + backward (Y; dX, dA, dB) of the seven LoRA
+linears of a LLaMA-7B-shaped decoder layer (q, k, v, o 4096x4096; gate, up
+11008x4096; down 4096x11008), NF4 + double-quantised weights, LoRA r=64,
+alpha=16, 8192 tokens (16 x 512) per linear; inputs resident in HBM.
+`value` = algorithmic TFLOP/s of the step: sum over linears of
+4 M N K (base forward + input gradient) + 6 M r (K + N) (LoRA), no dW.
+
+Legs timed in the same run (HBM-bound rows of the path):
+  quantize  NF4 + fp8 DQ of a stack of 65B-class layers (4 x 8192^2 +
+            3 x 22016x8192 weights per layer), 2.51587 B moved per weight
+  dequant   round trip of the same stack to bf16, 2.51587 B per weight
+  gemv      few-token forward (M = 1, 16) of 4096x4096 and 11008x4096 with
+            LoRA r=64, rotating over >= 1 GB of distinct weight sets
+  gemm512   forward at M = 512 (small-GEMM regime)
+  roofline  the dominant kernel (dequant-in-LDS MFMA GEMM, forward
+            orientation) over the seven layer shapes, timed with HIP events
+cpu_baseline: the float64 oracle (tests only, never on the product path) on
+a bounded sample of the step's work, on the host cores.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+Q_BYTES_PER_W = 2.0 + 0.5 + 1.0 / 64 + 4.0 / 16384   # read bf16, write codes, c2, c1
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", choices=["7b", "65b"], default="7b",
+                    help="layer shapes of the step: LLaMA-7B (default) or 65B-class")
+    ap.add_argument("--stack-layers", type=int, default=80, help="65B-class layers in the quantize leg")
+    ap.add_argument("--legs", default="roofline,quantize,gemv,gemm512",
+                    help="comma list of extra legs, or 'none'")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one MI355X: the path has no multi-GPU mode (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_nf4_quantized_12_amd as q
+    from bit_nf4_quantized_12_amd import synth
+
+    q.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    def timed(fn, reps):
+        s0 = torch.cuda.Event(enable_timing=True)
+        s1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s0.record(stream)
+        for _ in range(reps):
+            fn()
+        s1.record(stream)
+        torch.cuda.synchronize()
+        return s0.elapsed_time(s1) / 1e3
+
+    hidden, ffn = (4096, 11008) if args.config == "7b" else (8192, 22016)
+    M, r, alpha = 8192, 64, 16.0
+    s = alpha / r
+    shapes = synth.llama_linears(hidden, ffn)
+    gen_seed = 0
+
+    # ---- step inputs (device-generated, resident) --------------------------------------
+    log(f"preparing {args.config} layer: {[(n, N, K) for n, N, K in shapes]}, M={M}, r={r}")
+    lin = []
+    ws_bytes = 0
+    for i, (name, N, K) in enumerate(shapes):
+        base = 1000 * i
+        w = synth.device_normal_bf16(N * K, 0.02, gen_seed + base + 1, dev).view(N, K)
+        if args.config == "65b":  # Student-t(5) * 0.02 to stress absmax outliers
+            torch.manual_seed(gen_seed + base + 7)
+            t = torch.distributions.StudentT(torch.tensor(5.0, device=dev))
+            w = (t.sample((N, K)) * 0.02).to(torch.bfloat16)
+        W = q.quantize_weight(w.contiguous())
+        del w
+        A = synth.device_normal_bf16(r * K, 0.02, gen_seed + base + 2, dev).view(r, K)
+        B = synth.device_normal_bf16(N * r, 0.02, gen_seed + base + 3, dev).view(N, r)
+        X = synth.device_normal_bf16(M * K, 1.0, gen_seed + base + 4, dev).view(M, K)
+        dY = synth.device_normal_bf16(M * N, 1.0, gen_seed + base + 5, dev).view(M, N)
+        out = dict(Y=torch.empty(M, N, dtype=torch.bfloat16, device=dev),
+                   T=torch.empty(M, r, dtype=torch.float32, device=dev),
+                   dX=torch.empty(M, K, dtype=torch.bfloat16, device=dev),
+                   dA=torch.empty(r, K, dtype=torch.bfloat16, device=dev),
+                   dB=torch.empty(N, r, dtype=torch.bfloat16, device=dev))
+        lin.append(dict(name=name, N=N, K=K, W=W, A=A, B=B, X=X, dY=dY, out=out))
+        ws_bytes = max(ws_bytes, q.qlora_linear_workspace_bytes(M, N, K, r))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        for L in lin:
+            o = L["out"]
+            q.qlora_linear_fwd(L["W"], L["X"], L["A"], L["B"], s, Y=o["Y"], T=o["T"], workspace=ws)
+            q.qlora_linear_bwd(L["W"], L["X"], L["A"], L["B"], L["dY"], o["T"], s,
+                               dX=o["dX"], dA=o["dA"], dB=o["dB"], workspace=ws)
+
+    step_flops = sum(4.0 * M * L["N"] * L["K"] + 6.0 * M * r * (L["K"] + L["N"]) for L in lin)
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t_step = timed(step, args.steps)
+    ms_per_step = 1e3 * t_step / args.steps
+    tflops = step_flops * args.steps / t_step / 1e12
+    log(f"step: {ms_per_step:.3f} ms, {tflops:.1f} TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
+
+    legs = {}
+    want = set() if args.legs == "none" else set(args.legs.split(","))
+
+    # ---- roofline: dominant kernel, forward orientation over the 7 shapes ----------------
+    roofline = None
+    if "roofline" in want:
+        outs = [torch.empty(M, L["N"], dtype=torch.bfloat16, device=dev) for L in lin]
+
+        def base_pass():
+            for L, o in zip(lin, outs):
+                q.qlora_nf4_matmul(L["W"], L["X"], False, out=o)
+
+        base_pass()
+        reps = max(3, args.steps)
+        t = timed(base_pass, reps)
+        launches = reps * len(lin)
+        avg_s = t / launches
+        flops_per_launch = sum(2.0 * M * L["N"] * L["K"] for L in lin) / len(lin)
+        achieved = flops_per_launch / avg_s / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "kernel": "gemm_kernel<false,false> (qlora_nf4_matmul, X W~^T)",
+                    "avg_launch_us": round(avg_s * 1e6, 2), "launches": launches,
+                    "flops_per_launch": flops_per_launch}
+        log(f"roofline kernel: avg {avg_s * 1e6:.1f} us/launch, {achieved:.1f} TFLOP/s")
+        # input-gradient orientation, for reference
+        outs_t = [torch.empty(M, L["K"], dtype=torch.bfloat16, device=dev) for L in lin]
+
+        def base_pass_t():
+            for L, o in zip(lin, outs_t):
+                q.qlora_nf4_matmul(L["W"], L["dY"], True, out=o)
+
+        base_pass_t()
+        tt = timed(base_pass_t, reps)
+        legs["gemm_dx_orientation"] = {"tflops": round(flops_per_launch * launches / tt / 1e12, 2),
+                                       "avg_launch_us": round(tt / launches * 1e6, 2)}
+        del outs, outs_t
+
+    # ---- few-token forward (GEMV) and M = 512 ----------------------------------------------
+    if "gemv" in want or "gemm512" in want:
+        for N in (4096, 11008):
+            K = 4096
+            wbytes = 0.5 * N * K + N * K / 64 + 4 * N * K / 16384
+            nsets = max(2, int(-(-1.0e9 // wbytes)))
+            sets = []
+            for j in range(nsets):
+                w = synth.device_normal_bf16(N * K, 0.02, 50_000 + 97 * j + N, dev).view(N, K)
+                sets.append(dict(W=q.quantize_weight(w),
+                                 A=synth.device_normal_bf16(r * K, 0.02, 60_000 + j, dev).view(r, K),
+                                 B=synth.device_normal_bf16(N * r, 0.02, 70_000 + j, dev).view(N, r)))
+                del w
+            ms = ([1, 16] if "gemv" in want else []) + ([512] if "gemm512" in want else [])
+            for Mg in ms:
+                X = synth.device_normal_bf16(Mg * K, 1.0, 80_000 + Mg, dev).view(Mg, K)
+                Yo = torch.empty(Mg, N, dtype=torch.bfloat16, device=dev)
+                wsg = torch.empty(q.qlora_linear_workspace_bytes(Mg, N, K, r), dtype=torch.uint8, device=dev)
+
+                def run_all():
+                    for S in sets:
+                        q.qlora_linear_fwd(S["W"], X, S["A"], S["B"], s, save_T=False, Y=Yo, workspace=wsg)
+
+                run_all()
+                reps = 5
+                t = timed(run_all, reps)
+                per = t / (reps * nsets)
+                byts = wbytes + 2.0 * r * (K + N) + 2.0 * Mg * (K + N)
+                fl = 2.0 * Mg * N * K + 2.0 * Mg * r * (K + N)
+                key = f"{'gemv' if Mg <= 16 else 'gemm'}_M{Mg}_{N}x{K}"
+                legs[key] = {"us_per_call": round(per * 1e6, 2), "GB/s": round(byts / per / 1e9, 1),
+                             "hbm_frac": round(byts / per / 1e9 / PEAK_HBM_GBS, 4),
+                             "TFLOP/s": round(fl / per / 1e12, 2), "weight_sets": nsets}
+                log(f"{key}: {per * 1e6:.2f} us/call, {byts / per / 1e9:.0f} GB/s")
+            del sets
+            torch.cuda.empty_cache()
+
+    # ---- quantise + dequantise a 65B-class stack --------------------------------------------
+    if "quantize" in want:
+        per_layer = [(8192, 8192)] * 4 + [(22016, 8192)] * 3
+        free, _ = torch.cuda.mem_get_info(dev)
+        layer_bytes = sum(N * K for N, K in per_layer) * (2 + 0.5 + 1 / 64) + (64 << 20)
+        nl = max(1, min(args.stack_layers, int((free - (24 << 30)) // layer_bytes)))
+        log(f"quantize leg: {nl} layers of 65B-class weights")
+        stack = []
+        for li in range(nl):
+            for j, (N, K) in enumerate(per_layer):
+                w = synth.device_normal_bf16(N * K, 0.02, 1_000_000 + 10 * li + j, dev)
+                nc, nb, ng = q.storage_sizes(N * K)
+                stack.append((w, (torch.empty(nc, dtype=torch.uint8, device=dev),
+                                  torch.empty(nb, dtype=torch.uint8, device=dev),
+                                  torch.empty(ng, dtype=torch.float32, device=dev))))
+        params = sum(w.numel() for w, _ in stack)
+
+        def quant_all():
+            for w, o in stack:
+                q.qlora_quantize_nf4_dq(w, out=o)
+
+        quant_all()
+        t = timed(quant_all, 3)
+        per = t / 3
+        gbs = params * Q_BYTES_PER_W / per / 1e9
+        legs["quantize_65b_stack"] = {"layers": nl, "params": params, "ms_per_pass": round(per * 1e3, 3),
+                                      "GB/s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+        log(f"quantize: {nl} layers, {params / 1e9:.2f}e9 params, {per * 1e3:.2f} ms, {gbs:.0f} GB/s")
+        maxn = max(w.numel() for w, _ in stack)
+        # the bf16 input is no longer needed: free it before the round trip
+        stack = [(None, o, w.numel()) for w, o in stack]
+        torch.cuda.empty_cache()
+        buf = torch.empty(maxn, dtype=torch.bfloat16, device=dev)
+
+        def deq_all():
+            for _, (codes, c2, c1), n in stack:
+                q.qlora_dequant(codes, c2, c1, n, torch.bfloat16, out=buf[:n])
+
+        deq_all()
+        t = timed(deq_all, 3)
+        per = t / 3
+        gbs = params * Q_BYTES_PER_W / per / 1e9
+        legs["dequant_bf16_65b_stack"] = {"layers": nl, "ms_per_pass": round(per * 1e3, 3),
+                                          "GB/s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+        log(f"dequant bf16: {per * 1e3:.2f} ms, {gbs:.0f} GB/s")
+        del stack, buf
+        torch.cuda.empty_cache()
+
+    # ---- CPU oracle on a bounded sample of the step ---------------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.cpu_seconds, log)
+
+    line = {
+        "metric": "NF4-LoRA linear fwd+bwd TFLOP/s (% bf16 peak); quantize/GEMV HBM GB/s (%)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": ("LLaMA-7B-shaped decoder layer" if args.config == "7b" else "65B-class layer")
+                   + ": 7 NF4+DQ linears (q,k,v,o,gate,up,down), LoRA r=64 alpha=16 on each, "
+                   "8192 tokens, forward + backward (dX, dA, dB)",
+                   "hidden": hidden, "ffn": ffn, "tokens": M, "lora_r": r, "lora_alpha": alpha,
+                   "step_tflop": round(step_flops / 1e12, 4), "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "legs": legs,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(target_s, log):
+    """Time the float64 oracle (dequantise + forward + backward) on a sample of the step."""
+    import numpy as np
+
+    import oracle
+    from bit_nf4_quantized_12_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    N = K = 4096
+    r, s = 64, 16.0 / 64
+    case = synth.linear_case(1, N, K, r, seed=0, cfg=3)
+    w32 = case["W"][1]
+    pk, c2, c1 = oracle.quantize_nf4_dq(w32)   # the stored weight (load time, not timed)
+
+    def work(m):
+        g = np.random.default_rng(m)
+        X = g.standard_normal((m, K)).astype(np.float32)
+        dY = g.standard_normal((m, N)).astype(np.float32)
+        t0 = time.perf_counter()
+        Wt = oracle.bf16_round(oracle.dequant(pk, c2, c1, N * K)).reshape(N, K)
+        oracle.linear_fwd(X, Wt, case["A"][1], case["B"][1], s)
+        oracle.linear_bwd(X, Wt, case["A"][1], case["B"][1], dY, s)
+        return time.perf_counter() - t0
+
+    m = 256
+    t = work(m)
+    while t < target_s / 4 and m < 65536:
+        m *= 2
+        t = work(m)
+    flops = 4.0 * m * N * K + 6.0 * m * r * (K + N)
+    log(f"cpu oracle: {m} tokens of one 4096x4096 linear in {t:.2f} s on {threads} threads")
+    return {"value": round(flops / t / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"oracle dequant + fwd + bwd of one 4096x4096 NF4 linear (r=64) for {m} tokens "
+                      f"({flops / 1e9:.1f} GFLOP in {t:.2f} s)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -10,6 +10,7 @@ The function names are those of the C ABI (include/qlora.h):
 * ``qlora_nf4_levels()``
 * ``qlora_quantize_nf4_dq(w)``
 * ``qlora_dequant(codes, c2, c1, n, dtype)``
+* ``qlora_nf4_matmul(W, act, transposed)``
 * ``qlora_linear_workspace_bytes(M, N, K, r)``
 * ``qlora_linear_fwd(W, X, A, B, scale, ...)``
 * ``qlora_linear_bwd(W, X, A, B, dY, T, scale, ...)``
@@ -62,6 +63,7 @@ def load_library(path=LIB_PATH):
             "qlora_quantize_nf4_dq": ([vp, i64, vp, vp, vp, vp], i32),
             "qlora_dequant": ([vp, vp, vp, i64, i32, vp, vp], i32),
             "qlora_linear_workspace_bytes": ([i64, i64, i64, i64], sz),
+            "qlora_nf4_matmul": ([ctypes.POINTER(_Weight), vp, i64, i32, vp, vp], i32),
             "qlora_linear_fwd": ([ctypes.POINTER(_Weight), vp, vp, vp, i64, i64, f32, vp, vp, vp, sz, vp], i32),
             "qlora_linear_bwd": ([ctypes.POINTER(_Weight), vp, vp, vp, vp, vp, i64, i64, f32, vp, vp, vp, vp, sz, vp], i32),
             "qlora_status_string": ([i32], ctypes.c_char_p),
@@ -154,6 +156,20 @@ def qlora_dequant(codes, c2, c1, n, dtype=torch.float32, out=None):
         out = torch.empty(n, dtype=dtype, device=codes.device)
     _check(load_library().qlora_dequant(_ptr(codes), _ptr(c2), _ptr(c1), n, code, _ptr(out),
                                         _stream(codes.device)))
+    return out
+
+
+def qlora_nf4_matmul(W, act, transposed=False, out=None):
+    """Base product on the frozen weight: act W~^T ([M, N]) or, transposed, act W~ ([M, K])."""
+    _need(act, torch.bfloat16, "act")
+    M = act.shape[0]
+    if act.shape[1] != (W.rows if transposed else W.cols):
+        raise ValueError("act has the wrong number of columns")
+    if out is None:
+        out = torch.empty((M, W.cols if transposed else W.rows), dtype=torch.bfloat16, device=act.device)
+    w = _weight_struct(W)
+    _check(load_library().qlora_nf4_matmul(ctypes.byref(w), _ptr(act), M, 1 if transposed else 0,
+                                           _ptr(out), _stream(act.device)))
     return out
 
 

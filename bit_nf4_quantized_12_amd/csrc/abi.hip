@@ -153,6 +153,40 @@ int qlora_dequant(const uint8_t* codes, const uint8_t* c2_fp8, const float* c1, 
   }
 }
 
+int qlora_nf4_matmul(const qlora_nf4_weight* W, const void* act, int64_t M, int transposed,
+                     void* out, void* stream) {
+  if (!W || !act || !out || !W->codes || !W->c2_fp8 || !W->c1) return QLORA_ERR_NULL;
+  const int64_t N = W->rows, K = W->cols;
+  if (M < 1 || N < 1 || K < 64 || (K % 64) != 0) return QLORA_ERR_SHAPE;
+  if (transposed != 0 && transposed != 1) return QLORA_ERR_UNSUPPORTED;
+  if (M * std::max(N, K) >= (int64_t(1) << 31) || N * K >= (int64_t(1) << 40)) return QLORA_ERR_SHAPE;
+  if (!aligned(W->codes, 16) || !aligned(W->c2_fp8, 16) || !aligned(W->c1, 4) ||
+      !aligned(act, 16) || !aligned(out, 16))
+    return QLORA_ERR_ALIGN;
+  try {
+    if (tables_status() != 0) return QLORA_ERR_UNSUPPORTED;
+    GemmParams p;
+    p.act = static_cast<const uint16_t*>(act);
+    p.codes = W->codes;
+    p.c2 = W->c2_fp8;
+    p.c1 = W->c1;
+    p.wN = N;
+    p.wK = K;
+    p.lora_l = nullptr;
+    p.lora_r = nullptr;
+    p.rp = 0;
+    p.out = static_cast<uint16_t*>(out);
+    p.M = (int)M;
+    p.Nout = (int)(transposed ? K : N);
+    p.Kred = (int)(transposed ? N : K);
+    p.lv = host_levels();
+    QLORA_TRY(launch_gemm(p, transposed == 1, (hipStream_t)stream));
+    return QLORA_OK;
+  } catch (...) {
+    return QLORA_ERR_DEVICE;
+  }
+}
+
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
   if (M < 1 || N < 1 || K < 64 || (K % 64) != 0 || r < 1 || r > 256) return 0;
   if (M * std::max(N, K) >= (int64_t(1) << 31)) return 0;

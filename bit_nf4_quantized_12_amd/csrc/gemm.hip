@@ -49,7 +49,7 @@ __device__ __forceinline__ void dequant8(uint32_t word, float chat, const float*
   }
 }
 
-template <bool TW>
+template <bool TW, bool LORA>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
   __shared__ __align__(16) uint16_t sA[2][BM * LDP];
   __shared__ __align__(16) uint16_t sB[2][BN * LDP];
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
   }
 
   // LoRA epilogue: acc += lora_l[rows, :] . lora_r[cols, :]^T
-  if (p.lora_l != nullptr) {
+  if (LORA) {
     for (int kr = 0; kr < p.rp; kr += 32) {
       bf16x8 a[4], b[4];
 #pragma unroll
@@ -198,10 +198,14 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
 
 hipError_t launch_gemm(const GemmParams& p, bool transposed_w, hipStream_t s) {
   dim3 grid((p.Nout + BN - 1) / BN, (p.M + BM - 1) / BM);
-  if (transposed_w)
-    hipLaunchKernelGGL(gemm_kernel<true>, grid, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(gemm_kernel<false>, grid, dim3(256), 0, s, p);
+  const bool lora = p.lora_l != nullptr;
+  if (transposed_w) {
+    if (lora) hipLaunchKernelGGL((gemm_kernel<true, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((gemm_kernel<true, false>), grid, dim3(256), 0, s, p);
+  } else {
+    if (lora) hipLaunchKernelGGL((gemm_kernel<false, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((gemm_kernel<false, false>), grid, dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -102,6 +102,17 @@ int qlora_quantize_nf4_dq(const void* w_bf16, int64_t n, uint8_t* codes,
 int qlora_dequant(const uint8_t* codes, const uint8_t* c2_fp8, const float* c1,
                   int64_t n, int out_dtype, void* out, void* stream);
 
+/* Base product on the frozen weight alone (no adapters), dequantised in
+ * LDS: [P2] "Method": dequantise to BFloat16, then matrix multiplication in
+ * 16-bit (float32 accumulate, bf16 result).
+ *   transposed == 0:  out [M, N] = act [M, K] W~^T   (forward orientation)
+ *   transposed == 1:  out [M, K] = act [M, N] W~     (input-gradient orientation)
+ * W: host struct of device views (K % 64 == 0). act, out: device bf16,
+ * 16-byte aligned. One kernel launch, no workspace. Limits as for
+ * qlora_linear_fwd. Errors: NULL, SHAPE, ALIGN, DEVICE. */
+int qlora_nf4_matmul(const qlora_nf4_weight* W, const void* act, int64_t M, int transposed,
+                     void* out, void* stream);
+
 /* Workspace bytes needed by qlora_linear_fwd and qlora_linear_bwd for these
  * sizes (the larger of the two; 0 on invalid sizes). */
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
