@@ -44,7 +44,7 @@ struct Layout {
 
 Layout plan(int64_t M, int64_t N, int64_t K, int64_t r) {
   Layout L;
-  const int64_t rp = cdiv(r, 32) * 32;
+  const int64_t rp = cdiv(r, 64) * 64;
   // forward
   L.tsplit = proj_splits(M, K);
   size_t o = 0;
@@ -208,7 +208,7 @@ int qlora_linear_fwd(const qlora_nf4_weight* W, const void* X, const void* A, co
     if (tables_status() != 0) return QLORA_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     char* base = static_cast<char*>(ws);
-    const int rp = (int)(cdiv(r, 32) * 32);
+    const int rp = (int)(cdiv(r, 64) * 64);
     float* partT = reinterpret_cast<float*>(base + L.partT);
     float* T32 = T_save ? T_save : reinterpret_cast<float*>(base + L.T32);
     uint16_t* Ts = reinterpret_cast<uint16_t*>(base + L.Ts);
@@ -271,7 +271,7 @@ int qlora_linear_bwd(const qlora_nf4_weight* W, const void* X, const void* A, co
     if (tables_status() != 0) return QLORA_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     char* base = static_cast<char*>(ws);
-    const int rp = (int)(cdiv(r, 32) * 32);
+    const int rp = (int)(cdiv(r, 64) * 64);
     const uint16_t* Xh = static_cast<const uint16_t*>(X);
     const uint16_t* Ah = static_cast<const uint16_t*>(A);
     const uint16_t* Bh = static_cast<const uint16_t*>(B);

@@ -8,28 +8,89 @@
 // LoRA side follows "QLoRA: Efficient Fine-Tuning of Quantized Language
 // Models" (mbrenndoerfer.com), section "Low-Rank Adaptation (LoRA)".
 //
-// Tile 128 x 128 outputs, 64-deep reduction steps, 4 wave64 in 2 x 2, each
-// wave 64 x 64 outputs = 4 x 4 v_mfma_f32_16x16x32_bf16 tiles. Per step the
-// activation tile (bf16) is copied to LDS and the weight tile is unpacked
-// from 4-bit codes in registers, scaled by its block constant c^ and written
-// to LDS as bf16; LDS is double buffered (one barrier per step). Rows are
-// padded to 72 elements so the 16-lane column reads of the MFMA operands hit
-// 64 distinct banks.
+// Tile 256 x 256 outputs, 64-deep reduction steps (one NF4 block), 8 wave64
+// in 2 x 4, each wave 128 x 64 outputs = 8 x 4 v_mfma_f32_16x16x32_bf16
+// tiles (128 float32 accumulators per lane), two waves per SIMD: while one
+// wave keeps the matrix core busy the other issues its unpacking VALU work.
+// LDS holds two stages of the activation tile and of the weight tile (bf16,
+// 128 KB in all, 16-byte chunks XOR-swizzled per row so MFMA operand reads
+// are conflict free). The activation tile is streamed global -> LDS by
+// LDS-DMA (global_load_lds_dwordx4); no registers involved.
+//
+// Weight tiles are unpacked in registers: each thread owns half a block (32
+// codes) per step, builds the block's 16-entry table of bf16(q[c] * c^)
+// (16 multiplies, 8 conversions, 8 byte shuffles) and maps every code
+// through it with v_perm byte selects -- no LDS lookups, exact W~. Codes are
+// fetched two steps ahead, activations one step ahead.
+//
+// Workgroups are ordered so that each XCD (workgroup id mod 8) owns a
+// contiguous band of output tiles: the activation rows and weight columns
+// it streams stay in that XCD's L2.
 #include "launch.hpp"
 
 namespace qlora {
-
-
-
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64, LDP = 72;
+constexpr int BM = 256, BN = 256, BK = 64, NT = 512;
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// 16-entry table of one block, as byte planes: L[j] holds the low bytes of
+// entries 4j..4j+3, H[j] the high bytes.
+struct BlockTable {
+  uint32_t L[4], H[4];
+};
+
+__device__ __forceinline__ BlockTable make_table(float chat, const Levels& lv) {
+  uint32_t P[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) P[i] = pack_bf16(__fmul_rn(lv.q[2 * i], chat), __fmul_rn(lv.q[2 * i + 1], chat));
+  BlockTable t;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    t.L[j] = perm(P[2 * j + 1], P[2 * j], 0x06040200u);
+    t.H[j] = perm(P[2 * j + 1], P[2 * j], 0x07050301u);
+  }
+  return t;
+}
+
+// Look up the 8 codes of one word (element i in nibble i). Returns the bf16
+// of even elements in E (e0|e2<<16, e4|e6<<16) and odd ones in O (e1|e3<<16,
+// e5|e7<<16). Selector bytes: low 3 bits pick an entry inside a half table,
+// bit 3 picks the half.
+__device__ __forceinline__ void lookup8_split(uint32_t d, const BlockTable& t, uint32_t E[2],
+                                              uint32_t O[2]) {
+  const uint32_t se = d & 0x07070707u;
+  const uint32_t so = (d >> 4) & 0x07070707u;
+  const uint32_t ce = ((d >> 1) & 0x04040404u) | 0x03020100u;
+  const uint32_t co = ((d >> 5) & 0x04040404u) | 0x03020100u;
+  const uint32_t Le = perm(perm(t.L[3], t.L[2], se), perm(t.L[1], t.L[0], se), ce);
+  const uint32_t He = perm(perm(t.H[3], t.H[2], se), perm(t.H[1], t.H[0], se), ce);
+  const uint32_t Lo = perm(perm(t.L[3], t.L[2], so), perm(t.L[1], t.L[0], so), co);
+  const uint32_t Ho = perm(perm(t.H[3], t.H[2], so), perm(t.H[1], t.H[0], so), co);
+  E[0] = perm(He, Le, 0x05010400u);
+  E[1] = perm(He, Le, 0x07030602u);
+  O[0] = perm(Ho, Lo, 0x05010400u);
+  O[1] = perm(Ho, Lo, 0x07030602u);
+}
+
+// The same 8 weights as 4 packed pairs in natural order (e0|e1<<16, ...).
+__device__ __forceinline__ void lookup8(uint32_t d, const BlockTable& t, uint32_t out[4]) {
+  uint32_t E[2], O[2];
+  lookup8_split(d, t, E, O);
+  out[0] = perm(O[0], E[0], 0x05040100u);
+  out[1] = perm(O[0], E[0], 0x07060302u);
+  out[2] = perm(O[1], E[1], 0x05040100u);
+  out[3] = perm(O[1], E[1], 0x07060302u);
+}
 
 // 8 bf16 of row `row`, columns [col, col+8) of a [rows, ld] matrix; zeros
 // outside [0, nrows) x [0, ncols). `vec` means ld % 8 == 0 (16-byte rows).
 __device__ __forceinline__ uint4 load_row8(const uint16_t* __restrict__ base, int64_t ld, int row,
                                            int nrows, int col, int ncols, bool vec) {
-  if (row >= nrows) return make_uint4(0, 0, 0, 0);
+  if (row >= nrows || col >= ncols) return make_uint4(0, 0, 0, 0);
   const uint16_t* p = base + (int64_t)row * ld + col;
   if (vec && col + 8 <= ncols) return *reinterpret_cast<const uint4*>(p);
   uint32_t h[8];
@@ -38,154 +99,251 @@ __device__ __forceinline__ uint4 load_row8(const uint16_t* __restrict__ base, in
   return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
 }
 
-// 8 codes (one word) -> 8 bf16 of W~ = bf16(q[code] * chat), as 4 packed pairs.
-__device__ __forceinline__ void dequant8(uint32_t word, float chat, const float* __restrict__ sq,
-                                         uint32_t o[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float a = __fmul_rn(sq[(word >> (8 * i)) & 15u], chat);
-    const float b = __fmul_rn(sq[(word >> (8 * i + 4)) & 15u], chat);
-    o[i] = pack_bf16(a, b);
+// LDS tiles are 256 rows x 64 bf16 (128 B rows, no padding). The 16-byte
+// chunk c of row R is stored at chunk c ^ swz(R): the 16 rows read by one
+// MFMA operand fragment then land in 16 distinct 16-byte bank groups (64
+// banks), and every 8 consecutive rows in 8 distinct ones (32 banks).
+__device__ __forceinline__ int swz(int R) { return (R & 7) ^ ((R >> 3) & 1); }
+__device__ __forceinline__ int tile_off(int R, int c) { return R * 64 + 8 * (c ^ swz(R)); }
+
+// Half a weight block (32 codes) and its block constant.
+struct WHalf {
+  uint4 c;
+  float chat;
+};
+
+// Thread -> weight half-block of a step. Forward: thread t owns tile row
+// t >> 1 (weight row n0 + t/2), half t & 1 of the step's block. Input
+// gradient: lane l owns weight row k0 + l, wave w the block (w >> 1) of the
+// tile's four 64-column blocks, half w & 1.
+template <bool TW>
+__device__ __forceinline__ void wlane(int tid, int n0, int64_t& row, int64_t& col) {
+  const int w = tid >> 6, l = tid & 63;
+  if (!TW) {
+    row = n0 + (tid >> 1);
+    col = 32 * (tid & 1);
+  } else {
+    row = l;
+    col = n0 + 64 * (w >> 1) + 32 * (w & 1);
   }
 }
 
-template <bool TW, bool LORA>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
-  __shared__ __align__(16) uint16_t sA[2][BM * LDP];
-  __shared__ __align__(16) uint16_t sB[2][BN * LDP];
-  __shared__ float sq[16];
+// Unpack word q (weights 8q .. 8q+7 of this thread's half block) into the
+// weight tile of an LDS stage.
+template <bool TW>
+__device__ __forceinline__ void store_wword(uint32_t word, int q, const BlockTable& t,
+                                            uint16_t* __restrict__ dst, int tid) {
+  if (!TW) {
+    // tile row tid >> 1, reduction chunk 4 (tid & 1) + q
+    uint32_t o[4];
+    lookup8(word, t, o);
+    *reinterpret_cast<uint4*>(dst + tile_off(tid >> 1, 4 * (tid & 1) + q)) = make_uint4(o[0], o[1], o[2], o[3]);
+  } else {
+    // element e of the word is W~[k0 + l][n0 + 32 w + 8 q + e]: tile row
+    // 32 w + 8 q + e, reduction position l
+    const int w = tid >> 6, l = tid & 63;
+    uint32_t E[2], O[2];
+    lookup8_split(word, t, E, O);
+    const int r0 = 32 * w + 8 * q;
+    const uint16_t v[8] = {(uint16_t)E[0], (uint16_t)O[0], (uint16_t)(E[0] >> 16), (uint16_t)(O[0] >> 16),
+                           (uint16_t)E[1], (uint16_t)O[1], (uint16_t)(E[1] >> 16), (uint16_t)(O[1] >> 16)};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[tile_off(r0 + e, l >> 3) + (l & 7)] = v[e];
+  }
+}
+
+template <bool TW>
+__device__ __forceinline__ void store_whalf(const WHalf& h, const Levels& lv, uint16_t* __restrict__ dst, int tid) {
+  const BlockTable t = make_table(h.chat, lv);
+  const uint32_t words[4] = {h.c.x, h.c.y, h.c.z, h.c.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) store_wword<TW>(words[q], q, t, dst, tid);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+template <bool TW, bool LORA, bool VEC>
+__global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
+  extern __shared__ __align__(16) uint16_t smem[];
+  uint16_t* sA = smem;                // [2][BM * 64] activation tiles
+  uint16_t* sB = smem + 2 * BM * 64;  // [2][BN * 64] weight tiles
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63;
-  const int wm = w >> 1, wn = w & 1;
-  const int n0 = blockIdx.x * BN;  // output column tile
-  const int m0 = blockIdx.y * BM;  // output row tile
-  if (tid < 16) sq[tid] = p.lv.q[tid];
+  const int l = tid & 63;
+  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int wm = wu >> 2, wn = wu & 3;
 
-  const bool vec = (p.Kred & 7) == 0;
+  // XCD-aware tile order: workgroup g runs on XCD g % 8; XCD x owns the
+  // contiguous tile range [x * per, (x + 1) * per) in row-major tile order.
+  const int gn = (p.Nout + BN - 1) / BN;
+  const int gm = (p.M + BM - 1) / BM;
+  const int tiles = gn * gm;
+  const int per = (tiles + 7) / 8;
+  const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (t >= tiles) return;
+  const int m0 = (t / gn) * BM;
+  const int n0 = (t % gn) * BN;
   const int nk = (p.Kred + BK - 1) / BK;
 
-  uint4 ra[4];   // activation prefetch
-  uint4 rw;      // 32 codes
-  float chat;    // their block constant
-
-  auto prefetch = [&](int kt) {
-    const int k0 = kt * BK;
+  // ---- activation tile of step kt -> stage st --------------------------------------
+  // VEC (Kred % 64 == 0): LDS-DMA, 16 B per lane; instruction j of wave w
+  // fills rows 32 w + 8 j .. +7 (1 KB), lane i the physical chunk i & 7 of
+  // row 32 w + 8 j + (i >> 3), i.e. the logical chunk (i & 7) ^ swz(row).
+  // Rows past the end are clamped (they only feed unstored outputs); steps
+  // past the end reload the last step (prefetch overrun, never used). Lane
+  // byte offsets are fixed; the step moves a uniform base.
+  uint32_t xoff[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int id = tid + 256 * c;
-      const int row = id >> 3, col8 = id & 7;
-      ra[c] = load_row8(p.act, p.Kred, m0 + row, p.M, k0 + 8 * col8, p.Kred, vec);
-    }
-    int64_t n, col;
-    if (!TW) {  // W rows are output columns; one block per row per step
-      n = n0 + (tid >> 1);
-      col = k0 + 32 * (tid & 1);
-    } else {    // W rows are the reduction; 2 blocks per row per step
-      n = k0 + l;
-      col = n0 + 32 * w;
-    }
-    if (n < p.wN && col < p.wK) {
-      const int64_t e = n * p.wK + col;
-      rw = *reinterpret_cast<const uint4*>(p.codes + (e >> 1));
-      chat = block_scale(p.c2, p.c1, e >> 6);
+  for (int j = 0; j < 4; ++j) {
+    const int R = 32 * wu + 8 * j + (l >> 3);
+    const int row = min(m0 + R, p.M - 1);
+    xoff[j] = (uint32_t)(row * p.Kred + 8 * ((l & 7) ^ swz(R))) * 2u;
+  }
+  auto load_x = [&](int kt, int st) {
+    if (VEC) {
+      const int ke = min(kt, nk - 1);
+      const char* base = reinterpret_cast<const char*>(p.act) + (size_t)ke * (BK * 2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + xoff[j]),
+                                         (lds_void_t*)(sA + st * BM * 64 + (32 * wu + 8 * j) * 64), 16, 0, 0);
     } else {
-      rw = make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);
-      chat = 0.0f;
-    }
-  };
-
-  auto store_lds = [&](int st) {
+      const int k0 = kt * BK;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int id = tid + 256 * c;
-      const int row = id >> 3, col8 = id & 7;
-      *reinterpret_cast<uint4*>(&sA[st][row * LDP + 8 * col8]) = ra[c];
-    }
-    uint32_t o[16];
-    dequant8(rw.x, chat, sq, o + 0);
-    dequant8(rw.y, chat, sq, o + 4);
-    dequant8(rw.z, chat, sq, o + 8);
-    dequant8(rw.w, chat, sq, o + 12);
-    if (!TW) {
-      uint16_t* dst = &sB[st][(tid >> 1) * LDP + 32 * (tid & 1)];
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<uint4*>(dst + 8 * c) = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
-    } else {
-      // transpose into [output column][reduction]: element i of this lane's
-      // 32 is W~[k0 + l][n0 + 32 w + i]
-      uint16_t* dst = &sB[st][(32 * w) * LDP + l];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        dst[(2 * i) * LDP] = (uint16_t)(o[i] & 0xFFFFu);
-        dst[(2 * i + 1) * LDP] = (uint16_t)(o[i] >> 16);
+      for (int c = 0; c < 4; ++c) {
+        const int id = tid + NT * c;
+        const uint4 v = load_row8(p.act, p.Kred, m0 + (id >> 3), p.M, k0 + 8 * (id & 7), p.Kred, false);
+        *reinterpret_cast<uint4*>(&sA[st * BM * 64 + tile_off(id >> 3, id & 7)]) = v;
       }
     }
   };
 
-  f32x4 acc[4][4];
+  // ---- weight half-block of step kt -------------------------------------------------
+  int64_t wrow, wcol;
+  wlane<TW>(tid, n0, wrow, wcol);
+  const int64_t wstep = TW ? (int64_t)BK * p.wK : (int64_t)BK;  // elements per step
+  // VEC: every step is a full 64 reduction rows (forward: columns), so only
+  // the output side can run past the end: clamp it (unstored outputs).
+  const int64_t wbase = TW ? wrow * p.wK + min(wcol, p.wK - 32)
+                           : min(wrow, p.wN - 1) * p.wK + wcol;
+  auto load_w = [&](int kt) -> WHalf {
+    WHalf h;
+    if (VEC) {
+      const int ke = min(kt, nk - 1);
+      const int64_t e = (int64_t)ke * wstep + wbase;
+      h.c = *reinterpret_cast<const uint4*>(p.codes + (e >> 1));
+      h.chat = block_scale(p.c2, p.c1, e >> 6);
+    } else {
+      // general reduction length: a half block past the reduction end gets
+      // c^ = 0 (its unpacked weights are exact zeros, which zero the
+      // reduction tail); other out-of-range reads are clamped.
+      int64_t n = TW ? (int64_t)kt * BK + wrow : wrow;
+      int64_t col = TW ? wcol : (int64_t)kt * BK + wcol;
+      const bool ok = n < p.wN && col < p.wK;
+      n = min(n, p.wN - 1);
+      col = min(col, p.wK - 32);
+      const int64_t e = n * p.wK + col;
+      h.c = *reinterpret_cast<const uint4*>(p.codes + (e >> 1));
+      const float chat = block_scale(p.c2, p.c1, e >> 6);
+      h.chat = ok ? chat : 0.0f;
+    }
+    return h;
+  };
+
+  f32x4 acc[8][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  __syncthreads();  // sq ready
-  prefetch(0);
-  store_lds(0);
+  // prologue: stage 0 complete, codes of step 1 in flight
+  load_x(0, 0);
+  WHalf wnext = load_w(0);
+  store_whalf<TW>(wnext, p.lv, sB, tid);
+  wnext = load_w(1);
+  __builtin_amdgcn_s_waitcnt(0);  // stage 0 LDS-DMA landed (vmcnt = lgkmcnt = 0)
   __syncthreads();
+
+  const int arow = wm * 128 + (l & 15);
+  const int brow = wn * 64 + (l & 15);
+  // logical chunk of a fragment: 4 kk + (l >> 4); all fragment rows of a
+  // lane share swz(row) = swz(l & 15)
+  const int ck0 = 8 * ((0 + (l >> 4)) ^ swz(l & 15));
+  const int ck1 = 8 * ((4 + (l >> 4)) ^ swz(l & 15));
 
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
-    if (kt + 1 < nk) prefetch(kt + 1);
+    load_x(kt + 1, st ^ 1);
+    const WHalf wcur = wnext;
+    wnext = load_w(kt + 2);
+
+    const uint16_t* a_s = sA + st * BM * 64;
+    const uint16_t* b_s = sB + st * BN * 64;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 a[4], b[4];
+      const int ck = kk ? ck1 : ck0;
+      bf16x8 b[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = lds_load8(reinterpret_cast<const __bf16*>(&sA[st][(wm * 64 + 16 * i + (l & 15)) * LDP + 32 * kk + 8 * (l >> 4)]));
+      for (int j = 0; j < 4; ++j) b[j] = lds_load8(reinterpret_cast<const __bf16*>(b_s + (brow + 16 * j) * 64 + ck));
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = lds_load8(reinterpret_cast<const __bf16*>(&sB[st][(wn * 64 + 16 * j + (l & 15)) * LDP + 32 * kk + 8 * (l >> 4)]));
+      for (int i = 0; i < 8; ++i) {
+        const bf16x8 a = lds_load8(reinterpret_cast<const __bf16*>(a_s + (arow + 16 * i) * 64 + ck));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a, b[j], acc[i][j]);
+      }
     }
-    if (kt + 1 < nk) store_lds(st ^ 1);
+    // unpack the next weight tile into the other stage (free since the last
+    // barrier); steps past the end unpack a clamped block into an unused stage
+    store_whalf<TW>(wcur, p.lv, sB + (st ^ 1) * BN * 64, tid);
+    __builtin_amdgcn_s_waitcnt(0);  // this step's LDS-DMA and LDS writes are complete
     __syncthreads();
   }
 
-  // LoRA epilogue: acc += lora_l[rows, :] . lora_r[cols, :]^T
   if (LORA) {
-    for (int kr = 0; kr < p.rp; kr += 32) {
-      bf16x8 a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 v = load_row8(p.lora_l, p.rp, m0 + wm * 64 + 16 * i + (l & 15), p.M, kr + 8 * (l >> 4), p.rp, true);
-        a[i] = __builtin_bit_cast(bf16x8, v);
-      }
+    // acc += lora_l[rows, :] lora_r[cols, :]^T, 64 rank columns per step
+    // (rp is a multiple of 64, zero padded), staged through LDS stage 0 by
+    // LDS-DMA like the main loop; the loop ended on a barrier.
+    for (int kr = 0; kr < p.rp; kr += BK) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint4 v = load_row8(p.lora_r, p.rp, n0 + wn * 64 + 16 * j + (l & 15), p.Nout, kr + 8 * (l >> 4), p.rp, true);
-        b[j] = __builtin_bit_cast(bf16x8, v);
+        const int R = 32 * wu + 8 * j + (l >> 3);
+        const int c = (l & 7) ^ swz(R);
+        const int ra = min(m0 + R, p.M - 1), rb = min(n0 + R, p.Nout - 1);
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(p.lora_l + (int64_t)ra * p.rp + kr + 8 * c),
+                                         (lds_void_t*)(sA + (32 * wu + 8 * j) * 64), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(p.lora_r + (int64_t)rb * p.rp + kr + 8 * c),
+                                         (lds_void_t*)(sB + (32 * wu + 8 * j) * 64), 16, 0, 0);
       }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int kk = 0; kk < 2; ++kk) {
+        const int ck = kk ? ck1 : ck0;
+        bf16x8 b[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) b[j] = lds_load8(reinterpret_cast<const __bf16*>(sB + (brow + 16 * j) * 64 + ck));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const bf16x8 a = lds_load8(reinterpret_cast<const __bf16*>(sA + (arow + 16 * i) * 64 + ck));
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a, b[j], acc[i][j]);
+        }
+      }
+      __syncthreads();
     }
   }
 
+  // D layout of a 16 x 16 tile: lane holds rows 4 (l >> 4) + v, column l & 15
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int col = n0 + wn * 64 + 16 * j + (l & 15);
       if (col >= p.Nout) continue;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int row = m0 + wm * 64 + 16 * i + 4 * (l >> 4) + v;
+        const int row = m0 + wm * 128 + 16 * i + 4 * (l >> 4) + v;
         if (row < p.M) {
           const __bf16 h = (__bf16)acc[i][j][v];
           p.out[(int64_t)row * p.Nout + col] = __builtin_bit_cast(uint16_t, h);
@@ -194,19 +352,35 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
     }
 }
 
+constexpr size_t kSmemBytes = 2 * (BM + BN) * 64 * sizeof(uint16_t);
+
+template <bool TW, bool LORA, bool VEC>
+hipError_t launch_variant(const GemmParams& p, hipStream_t s) {
+  static bool configured = false;  // benign race: every thread sets the same value
+  if (!configured) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<TW, LORA, VEC>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmemBytes);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  const int tiles = ((p.Nout + BN - 1) / BN) * ((p.M + BM - 1) / BM);
+  const int grid = 8 * ((tiles + 7) / 8);
+  hipLaunchKernelGGL((gemm_kernel<TW, LORA, VEC>), dim3(grid), dim3(NT), kSmemBytes, s, p);
+  return hipGetLastError();
+}
+
+template <bool TW, bool LORA>
+hipError_t launch_rows(const GemmParams& p, hipStream_t s) {
+  // reductions in whole 64-element steps take the DMA / uniform-address path
+  return (p.Kred % BK == 0) ? launch_variant<TW, LORA, true>(p, s) : launch_variant<TW, LORA, false>(p, s);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmParams& p, bool transposed_w, hipStream_t s) {
-  dim3 grid((p.Nout + BN - 1) / BN, (p.M + BM - 1) / BM);
   const bool lora = p.lora_l != nullptr;
-  if (transposed_w) {
-    if (lora) hipLaunchKernelGGL((gemm_kernel<true, true>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((gemm_kernel<true, false>), grid, dim3(256), 0, s, p);
-  } else {
-    if (lora) hipLaunchKernelGGL((gemm_kernel<false, true>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((gemm_kernel<false, false>), grid, dim3(256), 0, s, p);
-  }
-  return hipGetLastError();
+  if (transposed_w) return lora ? launch_rows<true, true>(p, s) : launch_rows<true, false>(p, s);
+  return lora ? launch_rows<false, true>(p, s) : launch_rows<false, false>(p, s);
 }
 
 }  // namespace qlora

@@ -13,7 +13,7 @@ struct GemmParams {
   int64_t wN, wK;
   const uint16_t* lora_l;  // [M, rp] bf16 (scale folded in), or null
   const uint16_t* lora_r;  // [Nout, rp] bf16, or null
-  int rp;                  // multiple of 32
+  int rp;                  // multiple of 64, columns past r are zero
   uint16_t* out;           // [M, Nout] bf16
   int M, Nout, Kred;
   Levels lv;
