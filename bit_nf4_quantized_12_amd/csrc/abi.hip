@@ -22,9 +22,9 @@ inline int clampi(int64_t v, int64_t lo, int64_t hi) { return (int)(v < lo ? lo 
 
 // Reduction splits. Each aims at a few hundred workgroups on 256 CUs.
 inline int proj_splits(int64_t M, int64_t Kr) {
-  const int64_t max_split = std::max<int64_t>(1, Kr / 128);
-  if (M <= kGemvMaxM) return clampi(Kr / 256, 1, std::min<int64_t>(64, max_split));
-  return clampi(cdiv(256, cdiv(M, 64)), 1, std::min<int64_t>(32, max_split));
+  // ~512 workgroups of 64 rows; every slice keeps at least 4 steps of 64
+  const int64_t max_split = std::max<int64_t>(1, Kr / 256);
+  return clampi(cdiv(512, cdiv(M, 64)), 1, std::min<int64_t>(64, max_split));
 }
 inline int gemv_splits(int64_t N, int64_t K) {
   return clampi(cdiv(512, cdiv(N, 64)), 1, std::max<int64_t>(1, K / 512));

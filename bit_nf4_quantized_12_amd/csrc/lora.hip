@@ -100,6 +100,98 @@ __global__ __launch_bounds__(256) void proj_kernel(const uint16_t* __restrict__ 
   }
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+// Same product for Kr % 64 == 0 and rp == 64, streamed: a workgroup owns 64
+// rows of L and a reduction slice; each 64-deep step brings an L tile
+// (64 x 64) and an R tile (64 x 64) into LDS by LDS-DMA, four stages deep,
+// so that ~48 KB per workgroup are in flight. Wave w computes rows 16 w ..
+// 16 w + 15 against all 64 columns (4 MFMA tiles). Rows of R past r and
+// rows of L past M are clamped (their products land in columns / rows
+// nobody reads).
+constexpr int PJ_STAGES = 4;
+__device__ __forceinline__ int pj_swz(int R) { return (R & 7) ^ ((R >> 3) & 1); }
+
+__global__ __launch_bounds__(256) void proj_stream_kernel(const uint16_t* __restrict__ L,
+                                                           const uint16_t* __restrict__ R, int M,
+                                                           int Kr, int r, int kslice,
+                                                           float* __restrict__ part) {
+  __shared__ __align__(16) uint16_t sm[PJ_STAGES][2][64 * 64];
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m0 = blockIdx.x * 64;
+  const int ks = blockIdx.y;
+  const int kbeg = ks * kslice;
+  const int nsteps = max(0, min(Kr - kbeg, kslice)) / 64;
+
+  // DMA lanes: wave w fills rows 16 w .. 16 w + 15 of both tiles, two 1 KB
+  // instructions each; lane i -> row 16 w + 8 j + (i >> 3), physical chunk
+  // i & 7 = logical chunk (i & 7) ^ swz(row)
+  uint32_t loff[2], roff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = 16 * w + 8 * j + (l >> 3);
+    const int c = (l & 7) ^ pj_swz(row);
+    loff[j] = (uint32_t)(min(m0 + row, M - 1) * Kr + 8 * c) * 2u;
+    roff[j] = (uint32_t)(min(row, r - 1) * Kr + 8 * c) * 2u;
+  }
+  auto issue = [&](int step) {
+    const int slot = step % PJ_STAGES;
+    const int k = kbeg + 64 * min(step, nsteps - 1);
+    const char* lb = reinterpret_cast<const char*>(L) + (size_t)k * 2;
+    const char* rb = reinterpret_cast<const char*>(R) + (size_t)k * 2;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(lb + loff[j]), (lds_void_t*)(&sm[slot][0][(16 * w + 8 * j) * 64]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(rb + roff[j]), (lds_void_t*)(&sm[slot][1][(16 * w + 8 * j) * 64]), 16, 0, 0);
+    }
+  };
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int ck0 = 8 * ((0 + (l >> 4)) ^ pj_swz(l & 15));
+  const int ck1 = 8 * ((4 + (l >> 4)) ^ pj_swz(l & 15));
+
+  if (nsteps > 0) {
+#pragma unroll
+    for (int st = 0; st < PJ_STAGES - 1; ++st) issue(st);
+    for (int step = 0; step < nsteps; ++step) {
+      // 4 DMA instructions per thread per stage and no other vector memory
+      // op in the loop: the oldest stage has landed once at most
+      // (stages - 2) * 4 remain outstanding. LDS reads of the previous step
+      // are complete (lgkmcnt 0) before any wave passes the barrier and
+      // refills their slot. A plain s_barrier: __syncthreads would also wait
+      // for the in-flight prefetches.
+      __builtin_amdgcn_s_waitcnt((4 * (PJ_STAGES - 2)) | (7 << 4) | (0 << 8));
+      __builtin_amdgcn_s_barrier();
+      issue(step + PJ_STAGES - 1);  // refills the slot read one step ago
+      const uint16_t* lt = sm[step % PJ_STAGES][0];
+      const uint16_t* rt = sm[step % PJ_STAGES][1];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int ck = kk ? ck1 : ck0;
+        const bf16x8 a = lds_load8(reinterpret_cast<const __bf16*>(lt + (16 * w + (l & 15)) * 64 + ck));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8 b = lds_load8(reinterpret_cast<const __bf16*>(rt + (16 * j + (l & 15)) * 64 + ck));
+          acc[j] = mfma16(a, b, acc[j]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // drain the overrun prefetches before exit
+  }
+  float* dst = part + (int64_t)ks * M * 64;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = m0 + 16 * w + 4 * (l >> 4) + v;
+      if (row < M) dst[(int64_t)row * 64 + 16 * j + (l & 15)] = acc[j][v];
+    }
+}
+
 // Sum the reduction slices: P32 [M, r] float32 (may be null) and
 // Ps [M, rp] = bf16(scale * P), zero in columns r .. rp-1.
 __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ part, int nsplit,
@@ -262,6 +354,12 @@ __global__ __launch_bounds__(256) void relayout_kernel(const uint16_t* __restric
 
 hipError_t launch_proj(const uint16_t* L, const uint16_t* R, int M, int Kr, int r, int rp,
                        int nsplit, float* part, hipStream_t s) {
+  if (rp == 64 && Kr % 64 == 0) {
+    const int kslice = ((Kr + nsplit - 1) / nsplit + 63) / 64 * 64;
+    dim3 grid((M + 63) / 64, nsplit);
+    hipLaunchKernelGGL(proj_stream_kernel, grid, dim3(256), 0, s, L, R, M, Kr, r, kslice, part);
+    return hipGetLastError();
+  }
   const int kslice = ((Kr + nsplit - 1) / nsplit + 31) / 32 * 32;
   if (M <= 16) {
     dim3 grid(1, nsplit);
