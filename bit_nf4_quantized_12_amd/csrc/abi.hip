@@ -5,7 +5,7 @@
 #include <cmath>
 #include <new>
 
-#include "../../include/qlora.h"
+#include "qlora.h"
 #include "launch.hpp"
 
 
@@ -26,20 +26,18 @@ inline int proj_splits(int64_t M, int64_t Kr) {
   const int64_t max_split = std::max<int64_t>(1, Kr / 256);
   return clampi(cdiv(512, cdiv(M, 64)), 1, std::min<int64_t>(64, max_split));
 }
-inline int gemv_splits(int64_t N, int64_t K) {
-  return clampi(cdiv(512, cdiv(N, 64)), 1, std::max<int64_t>(1, K / 512));
-}
 inline int grad_splits(int64_t M, int64_t C, int64_t rp) {
+  // ~256 workgroups, each slice at least 8 steps of 64 rows
   const int64_t wgs = cdiv(C, 128) * cdiv(rp, 64);
-  return clampi(cdiv(512, wgs), 1, std::max<int64_t>(1, cdiv(M, 128)));
+  return clampi(cdiv(256, wgs), 1, std::max<int64_t>(1, cdiv(M, 512)));
 }
 
 struct Layout {
   // byte offsets into the workspace; kNone when unused
-  size_t partT = 0, T32 = 0, Ts = 0, Bpad = 0, gemvp = 0;            // forward
-  size_t Bt = 0, At = 0, partU = 0, U32 = 0, Us = 0, gpart = 0;      // backward
+  size_t partT = 0, T32 = 0, Ts = 0, Bpad = 0;                       // forward
+  size_t Bt = 0, At = 0, partU = 0, U32 = 0, Us = 0, PtH = 0, PtL = 0, gpart = 0;  // backward
   size_t fwd_total = 0, bwd_total = 0;
-  int tsplit = 1, gsplit = 1, usplit = 1, sA = 1, sB = 1;
+  int tsplit = 1, usplit = 1, sA = 1, sB = 1;
 };
 
 Layout plan(int64_t M, int64_t N, int64_t K, int64_t r) {
@@ -52,8 +50,6 @@ Layout plan(int64_t M, int64_t N, int64_t K, int64_t r) {
   L.T32 = o;   o = al256(o + (size_t)M * r * 4);
   L.Ts = o;    o = al256(o + (size_t)M * rp * 2);
   L.Bpad = o;  o = al256(o + (rp != r ? (size_t)N * rp * 2 : 0));
-  L.gsplit = gemv_splits(N, K);
-  L.gemvp = o; o = al256(o + (M <= kGemvMaxM ? (size_t)L.gsplit * M * N * 4 : 0));
   L.fwd_total = o;
   // backward (T recompute reuses the forward region [partT, Ts))
   L.usplit = proj_splits(M, N);
@@ -65,6 +61,9 @@ Layout plan(int64_t M, int64_t N, int64_t K, int64_t r) {
   L.Us = o;    o = al256(o + (size_t)M * rp * 2);
   L.sA = grad_splits(M, K, rp);
   L.sB = grad_splits(M, N, rp);
+  const int64_t Mp = cdiv(M, 64) * 64;
+  L.PtH = o;   o = al256(o + (size_t)rp * Mp * 2);
+  L.PtL = o;   o = al256(o + (size_t)rp * Mp * 2);
   L.gpart = o;
   o = al256(o + std::max((size_t)L.sA * rp * K * 4, (size_t)L.sB * rp * N * 4));
   L.bwd_total = o;
@@ -216,17 +215,17 @@ int qlora_linear_fwd(const qlora_nf4_weight* W, const void* X, const void* A, co
     const uint16_t* Ah = static_cast<const uint16_t*>(A);
     const uint16_t* Bh = static_cast<const uint16_t*>(B);
 
-    // T = X A^T, float32 [M, r]; Ts = bf16(scale * T) [M, rp]
+    // T = X A^T: split-K partials [tsplit][M][rp]
     QLORA_TRY(launch_proj(Xh, Ah, (int)M, (int)K, (int)r, rp, L.tsplit, partT, s));
-    QLORA_TRY(launch_finalize(partT, L.tsplit, (int)M, (int)r, rp, scale, T32, Ts, s));
-
     if (M <= kGemvMaxM) {
-      float* gp = reinterpret_cast<float*>(base + L.gemvp);
-      QLORA_TRY(launch_gemv(Xh, W->codes, W->c2_fp8, W->c1, (int)N, (int)K, (int)M, L.gsplit, gp, s));
-      QLORA_TRY(launch_gemv_finalize(gp, L.gsplit, (int)M, (int)N, T32, Bh, (int)r, scale,
-                                     static_cast<uint16_t*>(Y), s));
+      // few tokens: one weight-streaming kernel, which also sums the T
+      // partials, adds the LoRA term and writes T_save
+      QLORA_TRY(launch_gemv(Xh, W->codes, W->c2_fp8, W->c1, (int)N, (int)K, (int)M, partT, L.tsplit, rp,
+                            Bh, (int)r, scale, static_cast<uint16_t*>(Y), T_save, s));
       return QLORA_OK;
     }
+    // Ts = bf16(scale * T) [M, rp], T float32 [M, r]
+    QLORA_TRY(launch_finalize(partT, L.tsplit, (int)M, (int)r, rp, scale, T32, Ts, s));
     const uint16_t* Br = Bh;
     if (rp != r) {
       uint16_t* Bpad = reinterpret_cast<uint16_t*>(base + L.Bpad);
@@ -318,12 +317,27 @@ int qlora_linear_bwd(const qlora_nf4_weight* W, const void* X, const void* A, co
       p.lv = host_levels();
       QLORA_TRY(launch_gemm(p, true, s));
     }
-    // dA = s U^T X  [r, K]
-    QLORA_TRY(launch_grad(U32, Xh, (int)M, (int)K, (int)r, rp, L.sA, gpart, s));
-    QLORA_TRY(launch_grad_reduce(gpart, L.sA, (int)r, rp, (int)K, scale, false, static_cast<uint16_t*>(dA), s));
-    // dB = s dY^T T  [N, r], computed as (T^T dY)^T
-    QLORA_TRY(launch_grad(T, dYh, (int)M, (int)N, (int)r, rp, L.sB, gpart, s));
-    QLORA_TRY(launch_grad_reduce(gpart, L.sB, (int)r, rp, (int)N, scale, true, static_cast<uint16_t*>(dB), s));
+    // dA = s U^T X  [r, K];  dB = s dY^T T  [N, r], computed as (T^T dY)^T.
+    // Streamed kernels take U^T / T^T as bf16 hi + lo planes.
+    const int Mp = (int)(cdiv(M, 64) * 64);
+    uint16_t* PtH = reinterpret_cast<uint16_t*>(base + L.PtH);
+    uint16_t* PtL = reinterpret_cast<uint16_t*>(base + L.PtL);
+    if (K % 8 == 0) {
+      QLORA_TRY(launch_split_t(U32, (int)M, (int)r, rp, Mp, PtH, PtL, s));
+      QLORA_TRY(launch_grad_stream(PtH, PtL, Xh, (int)M, Mp, (int)K, rp, L.sA, false, gpart, s));
+      QLORA_TRY(launch_grad_reduce(gpart, L.sA, (int)r, rp, (int)K, scale, false, false, static_cast<uint16_t*>(dA), s));
+    } else {
+      QLORA_TRY(launch_grad(U32, Xh, (int)M, (int)K, (int)r, rp, L.sA, gpart, s));
+      QLORA_TRY(launch_grad_reduce(gpart, L.sA, (int)r, rp, (int)K, scale, false, false, static_cast<uint16_t*>(dA), s));
+    }
+    if (N % 8 == 0) {
+      QLORA_TRY(launch_split_t(T, (int)M, (int)r, rp, Mp, PtH, PtL, s));
+      QLORA_TRY(launch_grad_stream(PtH, PtL, dYh, (int)M, Mp, (int)N, rp, L.sB, true, gpart, s));
+      QLORA_TRY(launch_grad_reduce(gpart, L.sB, (int)r, rp, (int)N, scale, true, true, static_cast<uint16_t*>(dB), s));
+    } else {
+      QLORA_TRY(launch_grad(T, dYh, (int)M, (int)N, (int)r, rp, L.sB, gpart, s));
+      QLORA_TRY(launch_grad_reduce(gpart, L.sB, (int)r, rp, (int)N, scale, true, false, static_cast<uint16_t*>(dB), s));
+    }
     return QLORA_OK;
   } catch (...) {
     return QLORA_ERR_DEVICE;

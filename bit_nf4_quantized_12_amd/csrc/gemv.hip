@@ -4,117 +4,150 @@
 // "QLoRA: Efficient Finetuning of Quantized LLMs" (inquiringlines.com),
 // "Method": dequantise to BFloat16, multiply in 16-bit. With at most 16
 // tokens each weight is used at most 16 times, so the kernel streams the
-// codes once: every lane unpacks its 8 codes straight into the B operand of
-// a v_mfma_f32_16x16x32_bf16 (no LDS staging), the X rows (padded to 16 with
-// zeros) are the A operand. A workgroup owns 64 weight rows and a slice of
-// K; its 4 waves split the slice and meet in LDS. Slices are summed, and the
-// LoRA term added, by gemv_finalize.
+// codes exactly once, straight from HBM into registers:
+//
+//  * a workgroup (16 wave64) owns 16 weight rows over the whole of K; the
+//    waves take 128-column chunks round robin, two at a time with both
+//    chunks' loads in flight before any unpacking, and meet in LDS at the
+//    end, so there are no split-K partial sums in memory;
+//  * per chunk a lane loads 16 B of codes = 32 weights of its row (one
+//    global_load_dwordx4), unpacks them through its block's 16-entry bf16
+//    table with v_perm byte selects, and feeds four
+//    v_mfma_f32_16x16x32_bf16 with X rows (padded to 16 with zeros) as the
+//    A operand. The reduction order inside a chunk is permuted (MFMA k-slot
+//    8 g + e of product i is column 32 g + 8 i + e of the chunk), identically
+//    for both operands;
+//  * the epilogue sums the split-K partials of T = X A^T (LoRA projection,
+//    a separate small kernel) and adds s T B^T before the bf16 store.
 #include "launch.hpp"
 
 namespace qlora {
 namespace {
 
-__global__ __launch_bounds__(256) void gemv_kernel(const uint16_t* __restrict__ X,
-                                                    const uint8_t* __restrict__ codes,
-                                                    const uint8_t* __restrict__ c2,
-                                                    const float* __restrict__ c1, int N, int K,
-                                                    int M, int kslice, float* __restrict__ part,
-                                                    Levels lv) {
-  __shared__ float sq[16];
-  __shared__ float red[4][4][16][17];
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  if (tid < 16) sq[tid] = lv.q[tid];
-  __syncthreads();
-  const int n0 = blockIdx.x * 64;
-  const int ks = blockIdx.y;
-  const int kbeg = ks * kslice;
-  const int kend = min(K, kbeg + kslice);
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
 
-  f32x4 acc[4];
+// 16-entry bf16(q[c] * c^) table as byte planes (see the GEMM kernel).
+__device__ __forceinline__ void gv_table(float chat, const Levels& lv, uint32_t L[4], uint32_t H[4]) {
+  uint32_t P[8];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int xr = l & 15;
-  for (int k = kbeg + 32 * w; k < kend; k += 128) {
-    const int col = k + 8 * (l >> 4);
-    uint4 xv = make_uint4(0, 0, 0, 0);
-    if (xr < M) xv = *reinterpret_cast<const uint4*>(X + (int64_t)xr * K + col);
-    const bf16x8 a = __builtin_bit_cast(bf16x8, xv);
-    uint32_t cw[4];
-    float chat[4];
+  for (int i = 0; i < 8; ++i) P[i] = pack_bf16(__fmul_rn(lv.q[2 * i], chat), __fmul_rn(lv.q[2 * i + 1], chat));
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int n = n0 + 16 * t + (l & 15);
-      if (n < N) {
-        const int64_t e = (int64_t)n * K + col;
-        cw[t] = *reinterpret_cast<const uint32_t*>(codes + (e >> 1));
-        chat[t] = block_scale(c2, c1, e >> 6);
-      } else {
-        cw[t] = 0x77777777u;
-        chat[t] = 0.0f;
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      uint32_t o[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x0 = __fmul_rn(sq[(cw[t] >> (8 * i)) & 15u], chat[t]);
-        const float x1 = __fmul_rn(sq[(cw[t] >> (8 * i + 4)) & 15u], chat[t]);
-        o[i] = pack_bf16(x0, x1);
-      }
-      const bf16x8 b = __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
-      acc[t] = mfma16(a, b, acc[t]);
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) red[w][t][4 * (l >> 4) + v][l & 15] = acc[t][v];
-  __syncthreads();
-  // 4 tiles x 16 rows x 16 columns = 1024 sums
-  float* dst = part + (int64_t)ks * M * N;
-  for (int idx = tid; idx < 1024; idx += 256) {
-    const int t = idx >> 8, m = (idx >> 4) & 15, c = idx & 15;
-    const int n = n0 + 16 * t + c;
-    if (m < M && n < N)
-      dst[(int64_t)m * N + n] = red[0][t][m][c] + red[1][t][m][c] + red[2][t][m][c] + red[3][t][m][c];
+  for (int j = 0; j < 4; ++j) {
+    L[j] = perm(P[2 * j + 1], P[2 * j], 0x06040200u);
+    H[j] = perm(P[2 * j + 1], P[2 * j], 0x07050301u);
   }
 }
 
-// Y[m][n] = bf16( sum_s part[s][m][n] + scale * sum_j T[m][j] B[n][j] )
-__global__ __launch_bounds__(256) void gemv_finalize_kernel(const float* __restrict__ part,
-                                                             int nsplit, int M, int N,
-                                                             const float* __restrict__ T,
-                                                             const uint16_t* __restrict__ B, int r,
-                                                             float scale, uint16_t* __restrict__ Y) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)M * N) return;
-  const int64_t m = idx / N, n = idx % N;
-  float v = 0.0f;
-  for (int s = 0; s < nsplit; ++s) v += part[(int64_t)s * M * N + idx];
-  float lo = 0.0f;
-  for (int j = 0; j < r; ++j) lo = __builtin_fmaf(T[m * r + j], bf16lo(B[n * r + j]), lo);
-  const __bf16 h = (__bf16)(v + scale * lo);
-  Y[idx] = __builtin_bit_cast(uint16_t, h);
+// 8 codes -> 8 bf16 of W~ in natural order (4 packed pairs).
+__device__ __forceinline__ uint4 gv_lookup8(uint32_t d, const uint32_t L[4], const uint32_t H[4]) {
+  const uint32_t se = d & 0x07070707u;
+  const uint32_t so = (d >> 4) & 0x07070707u;
+  const uint32_t ce = ((d >> 1) & 0x04040404u) | 0x03020100u;
+  const uint32_t co = ((d >> 5) & 0x04040404u) | 0x03020100u;
+  const uint32_t Le = perm(perm(L[3], L[2], se), perm(L[1], L[0], se), ce);
+  const uint32_t He = perm(perm(H[3], H[2], se), perm(H[1], H[0], se), ce);
+  const uint32_t Lo = perm(perm(L[3], L[2], so), perm(L[1], L[0], so), co);
+  const uint32_t Ho = perm(perm(H[3], H[2], so), perm(H[1], H[0], so), co);
+  const uint32_t E0 = perm(He, Le, 0x05010400u), E1 = perm(He, Le, 0x07030602u);
+  const uint32_t O0 = perm(Ho, Lo, 0x05010400u), O1 = perm(Ho, Lo, 0x07030602u);
+  return make_uint4(perm(O0, E0, 0x05040100u), perm(O0, E0, 0x07060302u), perm(O1, E1, 0x05040100u),
+                    perm(O1, E1, 0x07060302u));
+}
+
+constexpr int GV_WAVES = 16;
+
+__global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
+    const uint16_t* __restrict__ X, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ c2,
+    const float* __restrict__ c1, int N, int K, int M, const float* __restrict__ tpart, int tsplit, int rp,
+    const uint16_t* __restrict__ B, int r, float scale, uint16_t* __restrict__ Y, float* __restrict__ T_out,
+    Levels lv) {
+  __shared__ float red[GV_WAVES][16][17];
+  __shared__ float sT[16][257];
+  __shared__ uint16_t sB[16 * 256];  // the workgroup's 16 rows of B
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * 16;
+  const int c = l & 15, g = l >> 4;
+  const int n = min(n0 + c, N - 1);  // rows past N: clamped read, result not stored
+  const bool xok = c < M;            // A-operand row = X row c (zero past M)
+  const uint16_t* xrow = X + (int64_t)min(c, M - 1) * K;
+  const int64_t rowe = (int64_t)n * K;
+  const int nchunks = (K + 127) / 128;
+
+  // this lane's 32 columns of chunk ch; K % 64 == 0, so only the upper half
+  // of the last chunk can be missing (clamped read, c^ = 0)
+  auto chunk_load = [&](int ch, uint4& cw, float& chat, int& kcc) {
+    const int kc = 128 * ch + 32 * g;
+    const bool kok = kc < K && ch < nchunks;
+    kcc = kok ? kc : K - 32;
+    const int64_t e = rowe + kcc;
+    cw = *reinterpret_cast<const uint4*>(codes + (e >> 1));
+    const float s2 = block_scale(c2, c1, e >> 6);
+    chat = kok ? s2 : 0.0f;
+  };
+  auto chunk_mma = [&](const uint4& cw, float chat, int kcc, f32x4& acc) {
+    uint32_t L[4], H[4];
+    gv_table(chat, lv, L, H);
+    const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint4 xv = *reinterpret_cast<const uint4*>(xrow + kcc + 8 * i);
+      xv = xok ? xv : make_uint4(0, 0, 0, 0);
+      const uint4 wv = gv_lookup8(words[i], L, H);
+      acc = mfma16(__builtin_bit_cast(bf16x8, xv), __builtin_bit_cast(bf16x8, wv), acc);
+    }
+  };
+
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int ch = w; ch < nchunks; ch += 2 * GV_WAVES) {
+    uint4 cw0, cw1;
+    float s0, s1;
+    int k0, k1;
+    chunk_load(ch, cw0, s0, k0);
+    chunk_load(ch + GV_WAVES, cw1, s1, k1);  // past the end: zero contribution
+    chunk_mma(cw0, s0, k0, acc);
+    chunk_mma(cw1, s1, k1, acc);
+  }
+  // D[m][n]: lane holds X rows 4 g + v, weight row c
+#pragma unroll
+  for (int v = 0; v < 4; ++v) red[w][4 * g + v][c] = acc[v];
+
+  // B rows n0 .. n0 + 15 (r columns each) into LDS
+  for (int idx = tid; idx < 16 * r; idx += 64 * GV_WAVES) {
+    const int rr = idx / r, j = idx % r;
+    sB[rr * r + j] = B[(int64_t)min(n0 + rr, N - 1) * r + j];
+  }
+  // T = sum of the split-K partials of X A^T, rows < M, columns < r
+  for (int idx = tid; idx < M * r; idx += 64 * GV_WAVES) {
+    const int m = idx / r, j = idx % r;
+    float s = 0.0f;
+    for (int k = 0; k < tsplit; ++k) s += tpart[((int64_t)k * M + m) * rp + j];
+    sT[m][j] = s;
+    if (blockIdx.x == 0 && T_out) T_out[(int64_t)m * r + j] = s;
+  }
+  __syncthreads();
+  // thread -> (m, row): m = tid >> 4, row = tid & 15 (first 256 threads)
+  const int m = tid >> 4, rr = tid & 15;
+  if (tid < 256 && m < M && n0 + rr < N) {
+    float y = 0.0f;
+#pragma unroll
+    for (int q = 0; q < GV_WAVES; ++q) y += red[q][m][rr];
+    float lo = 0.0f;
+    for (int j = 0; j < r; ++j) lo = __builtin_fmaf(sT[m][j], bf16lo(sB[rr * r + j]), lo);
+    const __bf16 h = (__bf16)(y + scale * lo);
+    Y[(int64_t)m * N + n0 + rr] = __builtin_bit_cast(uint16_t, h);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_gemv(const uint16_t* X, const uint8_t* codes, const uint8_t* c2, const float* c1,
-                       int N, int K, int M, int nsplit, float* part, hipStream_t s) {
-  const int kslice = ((K + nsplit - 1) / nsplit + 63) / 64 * 64;
-  dim3 grid((N + 63) / 64, nsplit);
-  hipLaunchKernelGGL(gemv_kernel, grid, dim3(256), 0, s, X, codes, c2, c1, N, K, M, kslice, part,
-                     host_levels());
-  return hipGetLastError();
-}
-
-hipError_t launch_gemv_finalize(const float* part, int nsplit, int M, int N, const float* T,
-                                const uint16_t* B, int r, float scale, uint16_t* Y, hipStream_t s) {
-  const int64_t total = (int64_t)M * N;
-  hipLaunchKernelGGL(gemv_finalize_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                     part, nsplit, M, N, T, B, r, scale, Y);
+                       int N, int K, int M, const float* tpart, int tsplit, int rp, const uint16_t* B,
+                       int r, float scale, uint16_t* Y, float* T_out, hipStream_t s) {
+  hipLaunchKernelGGL(gemv_kernel, dim3((N + 15) / 16), dim3(64 * GV_WAVES), 0, s, X, codes, c2, c1, N, K, M, tpart,
+                     tsplit, rp, B, r, scale, Y, T_out, host_levels());
   return hipGetLastError();
 }
 

@@ -31,13 +31,17 @@ hipError_t launch_finalize(const float* part, int nsplit, int M, int r, int rp, 
 hipError_t launch_grad(const float* P, const uint16_t* Q, int M, int C, int r, int rp, int nsplit,
                        float* part, hipStream_t s);
 hipError_t launch_grad_reduce(const float* part, int nsplit, int r, int rp, int C, float scale,
-                              bool transpose, uint16_t* out, hipStream_t s);
+                              bool transpose, bool part_trans, uint16_t* out, hipStream_t s);
+hipError_t launch_split_t(const float* P, int M, int r, int rp, int Mp, uint16_t* hi, uint16_t* lo,
+                          hipStream_t s);
+hipError_t launch_grad_stream(const uint16_t* PtH, const uint16_t* PtL, const uint16_t* Q, int M,
+                              int Mp, int C, int rp, int nsplit, bool trans, float* part,
+                              hipStream_t s);
 hipError_t launch_relayout(const uint16_t* in, int64_t rows_in, int64_t cols_in, int64_t ldi,
                            bool transpose, uint16_t* out, int64_t rows_out, int64_t cols_out,
                            int64_t ldo, hipStream_t s);
 hipError_t launch_gemv(const uint16_t* X, const uint8_t* codes, const uint8_t* c2, const float* c1,
-                       int N, int K, int M, int nsplit, float* part, hipStream_t s);
-hipError_t launch_gemv_finalize(const float* part, int nsplit, int M, int N, const float* T,
-                                const uint16_t* B, int r, float scale, uint16_t* Y, hipStream_t s);
+                       int N, int K, int M, const float* tpart, int tsplit, int rp, const uint16_t* B,
+                       int r, float scale, uint16_t* Y, float* T_out, hipStream_t s);
 
 }  // namespace qlora

@@ -320,17 +320,156 @@ __global__ __launch_bounds__(256) void grad_kernel(const float* __restrict__ P,
   }
 }
 
+// P [M, r] float32 -> Pt_hi, Pt_lo [rp, Mp] bf16 with Pt_hi + Pt_lo ~ P^T
+// to ~16 bits (hi = bf16(p), lo = bf16(p - hi)); zero for j >= r or m >= M.
+__global__ __launch_bounds__(256) void split_t_kernel(const float* __restrict__ P, int M, int r,
+                                                       int rp, int Mp, uint16_t* __restrict__ hi,
+                                                       uint16_t* __restrict__ lo) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)rp * Mp) return;
+  const int j = (int)(idx / Mp), m = (int)(idx % Mp);
+  const float v = (j < r && m < M) ? P[(int64_t)m * r + j] : 0.0f;
+  const __bf16 h = (__bf16)v;
+  const __bf16 e = (__bf16)(v - (float)h);
+  hi[idx] = __builtin_bit_cast(uint16_t, h);
+  lo[idx] = __builtin_bit_cast(uint16_t, e);
+}
+
+// part[s] = sum over the 64-row steps of slice s of Pt[j-chunk, m] Q[m, c]
+// for a 64 (j) x 128 (c) tile, C % 8 == 0. Three-stage LDS-DMA pipeline:
+// per step a Q tile (64 m x 128 c, natural 256 B rows), and the hi / lo Pt
+// tiles (64 j x 64 m, swizzled like the GEMM). Wave w owns j rows 16 w ..
+// 16 w + 15; its B operands are Q columns gathered along m by v_perm from
+// eight row reads (lane l covers columns 8 (l & 15) .. + 7, so MFMA column
+// slot l & 15 of product cc is column 8 (l & 15) + cc). Q rows past M are
+// clamped (Pt is zero there), columns past C too (unstored). The partial is
+// staged through LDS and written as [s][j][c] (TRANS false) or [s][c][j].
+constexpr int GR_STAGES = 3;
+template <bool TRANS>
+__global__ __launch_bounds__(256) void grad_stream_kernel(const uint16_t* __restrict__ PtH,
+                                                           const uint16_t* __restrict__ PtL,
+                                                           const uint16_t* __restrict__ Q, int M,
+                                                           int Mp, int C, int rp, int mchunk,
+                                                           float* __restrict__ part) {
+  extern __shared__ __align__(16) uint16_t gsm[];  // GR_STAGES x (Q 8192 | H 4096 | L 4096)
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cbase = blockIdx.x * 128;
+  const int s = blockIdx.y;
+  const int jc = blockIdx.z;
+  const int mbeg = s * mchunk;
+  const int nsteps = max(0, min(Mp - mbeg, mchunk)) / 64;
+  constexpr int STAGE = 8192 + 4096 + 4096;
+
+  // Q: lane covers tile rows 16 w + 4 q + (l >> 4), 16-byte chunk l & 15
+  const uint32_t qcol = (uint32_t)min(cbase + 8 * (l & 15), C - 8) * 2u;
+  const int qrow = 16 * w + (l >> 4);
+  uint32_t poff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row = 16 * w + 8 * q + (l >> 3);
+    poff[q] = (uint32_t)((jc * 64 + row) * Mp + mbeg + 8 * ((l & 7) ^ ((row & 7) ^ ((row >> 3) & 1)))) * 2u;
+  }
+  auto issue = [&](int step) {
+    uint16_t* st = gsm + (step % GR_STAGES) * STAGE;
+    const int ms = min(step, nsteps - 1) * 64;
+    const char* qb = reinterpret_cast<const char*>(Q);
+    const char* hb = reinterpret_cast<const char*>(PtH) + (size_t)ms * 2;
+    const char* lb = reinterpret_cast<const char*>(PtL) + (size_t)ms * 2;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = min(mbeg + ms + qrow + 4 * q, M - 1);  // rows past M: Pt is zero there
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(qb + ((uint32_t)row * (uint32_t)C * 2u + qcol)),
+                                       (lds_void_t*)(st + (16 * w + 4 * q) * 128), 16, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(hb + poff[q]), (lds_void_t*)(st + 8192 + (16 * w + 8 * q) * 64), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(lb + poff[q]), (lds_void_t*)(st + 12288 + (16 * w + 8 * q) * 64), 16, 0, 0);
+    }
+  };
+
+  f32x4 acc[8];
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc) acc[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int sw = (l & 7) ^ (((l & 15) >> 3) & 1);  // swz of A-fragment row l & 15
+  const int g = l >> 4;
+
+  if (nsteps > 0) {
+#pragma unroll
+    for (int st = 0; st < GR_STAGES - 1; ++st) issue(st);
+    for (int step = 0; step < nsteps; ++step) {
+      // 8 DMA instructions per thread per stage, nothing else in flight
+      __builtin_amdgcn_s_waitcnt((8 * (GR_STAGES - 2)) | (7 << 4) | (0 << 8));
+      __builtin_amdgcn_s_barrier();
+      issue(step + GR_STAGES - 1);
+      const uint16_t* st = gsm + (step % GR_STAGES) * STAGE;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int ch = 8 * ((4 * kk + g) ^ sw);
+        const bf16x8 ah = lds_load8(reinterpret_cast<const __bf16*>(st + 8192 + (16 * w + (l & 15)) * 64 + ch));
+        const bf16x8 al = lds_load8(reinterpret_cast<const __bf16*>(st + 12288 + (16 * w + (l & 15)) * 64 + ch));
+        uint4 rq[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          rq[i] = *reinterpret_cast<const uint4*>(st + (32 * kk + 8 * g + i) * 128 + 8 * (l & 15));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t lo4[4], hi4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t x0 = (&rq[2 * i].x)[e], x1 = (&rq[2 * i + 1].x)[e];
+            lo4[i] = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
+            hi4[i] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
+          }
+          const bf16x8 b0 = __builtin_bit_cast(bf16x8, make_uint4(lo4[0], lo4[1], lo4[2], lo4[3]));
+          const bf16x8 b1 = __builtin_bit_cast(bf16x8, make_uint4(hi4[0], hi4[1], hi4[2], hi4[3]));
+          acc[2 * e] = mfma16(ah, b0, acc[2 * e]);
+          acc[2 * e] = mfma16(al, b0, acc[2 * e]);
+          acc[2 * e + 1] = mfma16(ah, b1, acc[2 * e + 1]);
+          acc[2 * e + 1] = mfma16(al, b1, acc[2 * e + 1]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  // stage the 64 x 128 partial through LDS, then write it coalesced
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(gsm);  // [64 j][129]
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[(16 * w + 4 * g + v) * 129 + 8 * (l & 15) + cc] = acc[cc][v];
+  __syncthreads();
+  if (!TRANS) {
+    // part[s][j][c]: thread -> j = tid >> 2, 32 columns
+    const int j = tid >> 2, c0 = 32 * (tid & 3);
+    float* dst = part + ((int64_t)s * rp + jc * 64 + j) * C + cbase + c0;
+    for (int c = 0; c < 32; ++c)
+      if (cbase + c0 + c < C) dst[c] = red[j * 129 + c0 + c];
+  } else {
+    // part[s][c][j]: thread -> c = tid >> 1, 32 j values
+    const int c = tid >> 1, j0 = 32 * (tid & 1);
+    if (cbase + c < C) {
+      float* dst = part + ((int64_t)s * C + cbase + c) * rp + jc * 64 + j0;
+      for (int j = 0; j < 32; ++j) dst[j] = red[(j0 + j) * 129 + c];
+    }
+  }
+}
+
 // out = bf16(scale * sum_s part[s][j][c]); j < r, c < C. Transposed: out[c][j].
 __global__ __launch_bounds__(256) void grad_reduce_kernel(const float* __restrict__ part,
                                                            int nsplit, int r, int rp, int C,
-                                                           float scale, bool transpose,
+                                                           float scale, bool transpose, bool part_trans,
                                                            uint16_t* __restrict__ out) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)r * C) return;
   int64_t j, c;
   if (transpose) { c = idx / r; j = idx % r; } else { j = idx / C; c = idx % C; }
+  // partials are [s][j][c], or [s][c][j] when produced for a transposed output
+  const int64_t off = part_trans ? c * rp + j : j * C + c;
   float v = 0.0f;
-  for (int s = 0; s < nsplit; ++s) v += part[(int64_t)s * rp * C + j * C + c];
+  for (int s = 0; s < nsplit; ++s) v += part[(int64_t)s * rp * C + off];
   const __bf16 h = (__bf16)(scale * v);
   out[idx] = __builtin_bit_cast(uint16_t, h);
 }
@@ -388,10 +527,41 @@ hipError_t launch_grad(const float* P, const uint16_t* Q, int M, int C, int r, i
 }
 
 hipError_t launch_grad_reduce(const float* part, int nsplit, int r, int rp, int C, float scale,
-                              bool transpose, uint16_t* out, hipStream_t s) {
+                              bool transpose, bool part_trans, uint16_t* out, hipStream_t s) {
   const int64_t total = (int64_t)r * C;
   hipLaunchKernelGGL(grad_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                     part, nsplit, r, rp, C, scale, transpose, out);
+                     part, nsplit, r, rp, C, scale, transpose, part_trans, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_t(const float* P, int M, int r, int rp, int Mp, uint16_t* hi, uint16_t* lo,
+                          hipStream_t s) {
+  const int64_t total = (int64_t)rp * Mp;
+  hipLaunchKernelGGL(split_t_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, P, M, r,
+                     rp, Mp, hi, lo);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_stream(const uint16_t* PtH, const uint16_t* PtL, const uint16_t* Q, int M,
+                              int Mp, int C, int rp, int nsplit, bool trans, float* part,
+                              hipStream_t s) {
+  static bool configured = false;  // benign race: every thread sets the same value
+  const size_t smem = (size_t)GR_STAGES * (8192 + 4096 + 4096) * sizeof(uint16_t);
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&grad_stream_kernel<false>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&grad_stream_kernel<true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  const int mchunk = ((Mp + nsplit - 1) / nsplit + 63) / 64 * 64;
+  dim3 grid((C + 127) / 128, nsplit, rp / 64);
+  if (trans)
+    hipLaunchKernelGGL(grad_stream_kernel<true>, grid, dim3(256), smem, s, PtH, PtL, Q, M, Mp, C, rp, mchunk, part);
+  else
+    hipLaunchKernelGGL(grad_stream_kernel<false>, grid, dim3(256), smem, s, PtH, PtL, Q, M, Mp, C, rp, mchunk, part);
   return hipGetLastError();
 }
 
