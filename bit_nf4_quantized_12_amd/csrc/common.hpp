@@ -71,6 +71,12 @@ __device__ __forceinline__ float block_scale(const uint8_t* __restrict__ c2,
   return __fmul_rn(d, g);
 }
 
+// LDS tiles of 64 bf16 per row (128 B) store the 16-byte chunk c of row R
+// at chunk c ^ lds_swz(R). An MFMA operand fragment read (lane l: row l & 15,
+// chunk l >> 4, ds_read_b128) then needs no more LDS cycles than a linear
+// read on gfx950; an XOR with (R & 7) alone measured 2-way bank conflicts.
+__device__ __forceinline__ int lds_swz(int R) { return (R & 7) ^ (((R >> 1) & 1) << 2); }
+
 // Inline-tuned LDS load/store of 16 bytes.
 __device__ __forceinline__ bf16x8 lds_load8(const __bf16* p) {
   return *reinterpret_cast<const bf16x8*>(p);

@@ -99,11 +99,9 @@ __device__ __forceinline__ uint4 load_row8(const uint16_t* __restrict__ base, in
   return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
 }
 
-// LDS tiles are 256 rows x 64 bf16 (128 B rows, no padding). The 16-byte
-// chunk c of row R is stored at chunk c ^ swz(R): the 16 rows read by one
-// MFMA operand fragment then land in 16 distinct 16-byte bank groups (64
-// banks), and every 8 consecutive rows in 8 distinct ones (32 banks).
-__device__ __forceinline__ int swz(int R) { return (R & 7) ^ ((R >> 3) & 1); }
+// LDS tiles are 256 rows x 64 bf16 (128 B rows, no padding), 16-byte chunks
+// XOR-swizzled per row (lds_swz).
+__device__ __forceinline__ int swz(int R) { return lds_swz(R); }
 __device__ __forceinline__ int tile_off(int R, int c) { return R * 64 + 8 * (c ^ swz(R)); }
 
 // Half a weight block (32 codes) and its block constant.

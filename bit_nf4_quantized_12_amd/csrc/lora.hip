@@ -111,7 +111,7 @@ typedef __attribute__((address_space(1))) void gbl_void_t;
 // rows of L past M are clamped (their products land in columns / rows
 // nobody reads).
 constexpr int PJ_STAGES = 4;
-__device__ __forceinline__ int pj_swz(int R) { return (R & 7) ^ ((R >> 3) & 1); }
+__device__ __forceinline__ int pj_swz(int R) { return lds_swz(R); }
 
 __global__ __launch_bounds__(256) void proj_stream_kernel(const uint16_t* __restrict__ L,
                                                            const uint16_t* __restrict__ R, int M,
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(256) void grad_stream_kernel(const uint16_t* __rest
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int row = 16 * w + 8 * q + (l >> 3);
-    poff[q] = (uint32_t)((jc * 64 + row) * Mp + mbeg + 8 * ((l & 7) ^ ((row & 7) ^ ((row >> 3) & 1)))) * 2u;
+    poff[q] = (uint32_t)((jc * 64 + row) * Mp + mbeg + 8 * ((l & 7) ^ lds_swz(row))) * 2u;
   }
   auto issue = [&](int step) {
     uint16_t* st = gsm + (step % GR_STAGES) * STAGE;
@@ -392,7 +392,7 @@ __global__ __launch_bounds__(256) void grad_stream_kernel(const uint16_t* __rest
   f32x4 acc[8];
 #pragma unroll
   for (int cc = 0; cc < 8; ++cc) acc[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int sw = (l & 7) ^ (((l & 15) >> 3) & 1);  // swz of A-fragment row l & 15
+  const int sw = lds_swz(l & 15);  // swizzle of A-fragment row l & 15
   const int g = l >> 4;
 
   if (nsteps > 0) {
