@@ -35,7 +35,7 @@ inline int grad_splits(int64_t M, int64_t C, int64_t rp) {
 struct Layout {
   // byte offsets into the workspace; kNone when unused
   size_t partT = 0, T32 = 0, Ts = 0, Bpad = 0;                       // forward
-  size_t Bt = 0, At = 0, partU = 0, U32 = 0, Us = 0, PtH = 0, PtL = 0, gpart = 0;  // backward
+  size_t Bt = 0, At = 0, partU = 0, U32 = 0, PtH = 0, PtL = 0, gpart = 0;  // backward
   size_t fwd_total = 0, bwd_total = 0;
   int tsplit = 1, usplit = 1, sA = 1, sB = 1;
 };
@@ -58,7 +58,6 @@ Layout plan(int64_t M, int64_t N, int64_t K, int64_t r) {
   L.At = o;    o = al256(o + (size_t)K * rp * 2);
   L.partU = o; o = al256(o + (size_t)L.usplit * M * rp * 4);
   L.U32 = o;   o = al256(o + (size_t)M * r * 4);
-  L.Us = o;    o = al256(o + (size_t)M * rp * 2);
   L.sA = grad_splits(M, K, rp);
   L.sB = grad_splits(M, N, rp);
   const int64_t Mp = cdiv(M, 64) * 64;
@@ -225,7 +224,7 @@ int qlora_linear_fwd(const qlora_nf4_weight* W, const void* X, const void* A, co
       return QLORA_OK;
     }
     // Ts = bf16(scale * T) [M, rp], T float32 [M, r]
-    QLORA_TRY(launch_finalize(partT, L.tsplit, (int)M, (int)r, rp, scale, T32, Ts, s));
+    QLORA_TRY(launch_finalize(partT, L.tsplit, (int)M, (int)M, (int)r, rp, scale, T32, Ts, nullptr, s));
     const uint16_t* Br = Bh;
     if (rp != r) {
       uint16_t* Bpad = reinterpret_cast<uint16_t*>(base + L.Bpad);
@@ -279,7 +278,11 @@ int qlora_linear_bwd(const qlora_nf4_weight* W, const void* X, const void* A, co
     uint16_t* At = reinterpret_cast<uint16_t*>(base + L.At);
     float* partU = reinterpret_cast<float*>(base + L.partU);
     float* U32 = reinterpret_cast<float*>(base + L.U32);
-    uint16_t* Us = reinterpret_cast<uint16_t*>(base + L.Us);
+    // hi / lo bf16 planes [Mp, rp] of s U, later of s T (rows past M zero);
+    // the hi plane of s U is also the row operand of the dX epilogue
+    const int Mp = (int)(cdiv(M, 64) * 64);
+    uint16_t* PtH = reinterpret_cast<uint16_t*>(base + L.PtH);
+    uint16_t* PtL = reinterpret_cast<uint16_t*>(base + L.PtL);
     float* gpart = reinterpret_cast<float*>(base + L.gpart);
 
     // T (float32 [M, r]): saved by the forward, or recomputed
@@ -289,13 +292,13 @@ int qlora_linear_bwd(const qlora_nf4_weight* W, const void* X, const void* A, co
       float* T32 = reinterpret_cast<float*>(base + L.T32);
       uint16_t* Ts = reinterpret_cast<uint16_t*>(base + L.Ts);
       QLORA_TRY(launch_proj(Xh, Ah, (int)M, (int)K, (int)r, rp, L.tsplit, partT, s));
-      QLORA_TRY(launch_finalize(partT, L.tsplit, (int)M, (int)r, rp, 1.0f, T32, Ts, s));
+      QLORA_TRY(launch_finalize(partT, L.tsplit, (int)M, (int)M, (int)r, rp, 1.0f, T32, Ts, nullptr, s));
       T = T32;
     }
     // U = dY B: B^T [r, N] is the row operand of the projection
     QLORA_TRY(launch_relayout(Bh, N, r, r, true, Bt, r, N, N, s));
     QLORA_TRY(launch_proj(dYh, Bt, (int)M, (int)N, (int)r, rp, L.usplit, partU, s));
-    QLORA_TRY(launch_finalize(partU, L.usplit, (int)M, (int)r, rp, scale, U32, Us, s));
+    QLORA_TRY(launch_finalize(partU, L.usplit, (int)M, Mp, (int)r, rp, scale, U32, PtH, PtL, s));
 
     if (dX) {
       // dX = dY W~ + (s U) A; A^T [K, rp] is the column operand of the epilogue
@@ -307,7 +310,7 @@ int qlora_linear_bwd(const qlora_nf4_weight* W, const void* X, const void* A, co
       p.c1 = W->c1;
       p.wN = N;
       p.wK = K;
-      p.lora_l = Us;
+      p.lora_l = PtH;
       p.lora_r = At;
       p.rp = rp;
       p.out = static_cast<uint16_t*>(dX);
@@ -317,23 +320,14 @@ int qlora_linear_bwd(const qlora_nf4_weight* W, const void* X, const void* A, co
       p.lv = host_levels();
       QLORA_TRY(launch_gemm(p, true, s));
     }
-    // dA = s U^T X  [r, K];  dB = s dY^T T  [N, r], computed as (T^T dY)^T.
-    // Streamed kernels take U^T / T^T as bf16 hi + lo planes.
-    const int Mp = (int)(cdiv(M, 64) * 64);
-    uint16_t* PtH = reinterpret_cast<uint16_t*>(base + L.PtH);
-    uint16_t* PtL = reinterpret_cast<uint16_t*>(base + L.PtL);
-    if (K % 8 == 0) {
-      QLORA_TRY(launch_split_t(U32, (int)M, (int)r, rp, Mp, PtH, PtL, s));
-      QLORA_TRY(launch_grad_stream(PtH, PtL, Xh, (int)M, Mp, (int)K, rp, L.sA, false, gpart, s));
-      QLORA_TRY(launch_grad_reduce(gpart, L.sA, (int)r, rp, (int)K, scale, false, false, static_cast<uint16_t*>(dA), s));
-    } else {
-      QLORA_TRY(launch_grad(U32, Xh, (int)M, (int)K, (int)r, rp, L.sA, gpart, s));
-      QLORA_TRY(launch_grad_reduce(gpart, L.sA, (int)r, rp, (int)K, scale, false, false, static_cast<uint16_t*>(dA), s));
-    }
+    // dA = (s U)^T X  [r, K] (K % 64 == 0); dB = s dY^T T  [N, r], computed as
+    // ((s T)^T dY)^T. The rank-r factor enters as its hi + lo bf16 planes.
+    QLORA_TRY(launch_grad_tr(PtH, PtL, Xh, (int)M, Mp, (int)K, rp, L.sA, false, gpart, s));
+    QLORA_TRY(launch_grad_reduce(gpart, L.sA, (int)r, rp, (int)K, 1.0f, false, false, static_cast<uint16_t*>(dA), s));
     if (N % 8 == 0) {
-      QLORA_TRY(launch_split_t(T, (int)M, (int)r, rp, Mp, PtH, PtL, s));
-      QLORA_TRY(launch_grad_stream(PtH, PtL, dYh, (int)M, Mp, (int)N, rp, L.sB, true, gpart, s));
-      QLORA_TRY(launch_grad_reduce(gpart, L.sB, (int)r, rp, (int)N, scale, true, true, static_cast<uint16_t*>(dB), s));
+      QLORA_TRY(launch_split_rows(T, (int)M, Mp, (int)r, rp, scale, PtH, PtL, s));
+      QLORA_TRY(launch_grad_tr(PtH, PtL, dYh, (int)M, Mp, (int)N, rp, L.sB, true, gpart, s));
+      QLORA_TRY(launch_grad_reduce(gpart, L.sB, (int)r, rp, (int)N, 1.0f, true, true, static_cast<uint16_t*>(dB), s));
     } else {
       QLORA_TRY(launch_grad(T, dYh, (int)M, (int)N, (int)r, rp, L.sB, gpart, s));
       QLORA_TRY(launch_grad_reduce(gpart, L.sB, (int)r, rp, (int)N, scale, true, false, static_cast<uint16_t*>(dB), s));

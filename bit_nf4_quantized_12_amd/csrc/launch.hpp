@@ -26,17 +26,16 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* c2, const float* 
 hipError_t launch_gemm(const GemmParams& p, bool transposed_w, hipStream_t s);
 hipError_t launch_proj(const uint16_t* L, const uint16_t* R, int M, int Kr, int r, int rp,
                        int nsplit, float* part, hipStream_t s);
-hipError_t launch_finalize(const float* part, int nsplit, int M, int r, int rp, float scale,
-                           float* P32, uint16_t* Ps, hipStream_t s);
+hipError_t launch_finalize(const float* part, int nsplit, int M, int Mp, int r, int rp, float scale,
+                           float* P32, uint16_t* Ph, uint16_t* Pl, hipStream_t s);
 hipError_t launch_grad(const float* P, const uint16_t* Q, int M, int C, int r, int rp, int nsplit,
                        float* part, hipStream_t s);
 hipError_t launch_grad_reduce(const float* part, int nsplit, int r, int rp, int C, float scale,
                               bool transpose, bool part_trans, uint16_t* out, hipStream_t s);
-hipError_t launch_split_t(const float* P, int M, int r, int rp, int Mp, uint16_t* hi, uint16_t* lo,
-                          hipStream_t s);
-hipError_t launch_grad_stream(const uint16_t* PtH, const uint16_t* PtL, const uint16_t* Q, int M,
-                              int Mp, int C, int rp, int nsplit, bool trans, float* part,
-                              hipStream_t s);
+hipError_t launch_split_rows(const float* P, int M, int Mp, int r, int rp, float scale, uint16_t* hi,
+                             uint16_t* lo, hipStream_t s);
+hipError_t launch_grad_tr(const uint16_t* Ph, const uint16_t* Pl, const uint16_t* Q, int M, int Mp, int C,
+                          int rp, int nsplit, bool trans, float* part, hipStream_t s);
 hipError_t launch_relayout(const uint16_t* in, int64_t rows_in, int64_t cols_in, int64_t ldi,
                            bool transpose, uint16_t* out, int64_t rows_out, int64_t cols_out,
                            int64_t ldo, hipStream_t s);

@@ -195,21 +195,25 @@ __global__ __launch_bounds__(256) void proj_stream_kernel(const uint16_t* __rest
 // Sum the reduction slices: P32 [M, r] float32 (may be null) and
 // Ps [M, rp] = bf16(scale * P), zero in columns r .. rp-1.
 __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ part, int nsplit,
-                                                        int M, int r, int rp, float scale,
+                                                        int M, int Mp, int r, int rp, float scale,
                                                         float* __restrict__ P32,
-                                                        uint16_t* __restrict__ Ps) {
+                                                        uint16_t* __restrict__ Ph,
+                                                        uint16_t* __restrict__ Pl) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)M * rp) return;
+  if (idx >= (int64_t)Mp * rp) return;
   const int64_t m = idx / rp;
   const int j = (int)(idx % rp);
-  float v = 0.0f;
-  for (int s = 0; s < nsplit; ++s) v += part[(int64_t)s * M * rp + idx];
-  if (j < r) {
+  if (m < M && j < r) {
+    float v = 0.0f;
+    for (int s = 0; s < nsplit; ++s) v += part[(int64_t)s * M * rp + idx];
     if (P32) P32[m * r + j] = v;
-    const __bf16 h = (__bf16)(scale * v);
-    Ps[idx] = __builtin_bit_cast(uint16_t, h);
+    const float sv = scale * v;
+    const __bf16 h = (__bf16)sv;
+    Ph[idx] = __builtin_bit_cast(uint16_t, h);
+    if (Pl) Pl[idx] = __builtin_bit_cast(uint16_t, (__bf16)(sv - (float)h));
   } else {
-    Ps[idx] = 0;
+    Ph[idx] = 0;
+    if (Pl) Pl[idx] = 0;
   }
 }
 
@@ -322,137 +326,178 @@ __global__ __launch_bounds__(256) void grad_kernel(const float* __restrict__ P,
 
 // P [M, r] float32 -> Pt_hi, Pt_lo [rp, Mp] bf16 with Pt_hi + Pt_lo ~ P^T
 // to ~16 bits (hi = bf16(p), lo = bf16(p - hi)); zero for j >= r or m >= M.
-__global__ __launch_bounds__(256) void split_t_kernel(const float* __restrict__ P, int M, int r,
-                                                       int rp, int Mp, uint16_t* __restrict__ hi,
-                                                       uint16_t* __restrict__ lo) {
+// hi / lo bf16 planes [Mp, rp] of scale * P, P float32 [M, r]; zero outside.
+__global__ __launch_bounds__(256) void split_rows_kernel(const float* __restrict__ P, int M, int Mp,
+                                                          int r, int rp, float scale,
+                                                          uint16_t* __restrict__ hi,
+                                                          uint16_t* __restrict__ lo) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)rp * Mp) return;
-  const int j = (int)(idx / Mp), m = (int)(idx % Mp);
-  const float v = (j < r && m < M) ? P[(int64_t)m * r + j] : 0.0f;
+  if (idx >= (int64_t)Mp * rp) return;
+  const int64_t m = idx / rp;
+  const int j = (int)(idx % rp);
+  const float v = (m < M && j < r) ? scale * P[m * r + j] : 0.0f;
   const __bf16 h = (__bf16)v;
-  const __bf16 e = (__bf16)(v - (float)h);
   hi[idx] = __builtin_bit_cast(uint16_t, h);
-  lo[idx] = __builtin_bit_cast(uint16_t, e);
+  lo[idx] = __builtin_bit_cast(uint16_t, (__bf16)(v - (float)h));
 }
 
-// part[s] = sum over the 64-row steps of slice s of Pt[j-chunk, m] Q[m, c]
-// for a 64 (j) x 128 (c) tile, C % 8 == 0. Three-stage LDS-DMA pipeline:
-// per step a Q tile (64 m x 128 c, natural 256 B rows), and the hi / lo Pt
-// tiles (64 j x 64 m, swizzled like the GEMM). Wave w owns j rows 16 w ..
-// 16 w + 15; its B operands are Q columns gathered along m by v_perm from
-// eight row reads (lane l covers columns 8 (l & 15) .. + 7, so MFMA column
-// slot l & 15 of product cc is column 8 (l & 15) + cc). Q rows past M are
-// clamped (Pt is zero there), columns past C too (unstored). The partial is
-// staged through LDS and written as [s][j][c] (TRANS false) or [s][c][j].
-constexpr int GR_STAGES = 3;
+// part[s][j][c] (TRANS: part[s][c][j]) = sum over the rows m of slice s of
+// P[m][j] Q[m][c], with P = hi + lo, two bf16 planes [Mp, rp] (rows past M
+// zero) and Q [M, C] bf16, C % 8 == 0. A workgroup (8 waves) owns 64 j
+// (block jc) x 128 c; each 64-row step brings the Q tile (64 x 128, 256 B
+// rows) and the two P tiles (64 x 64, 128 B rows) into LDS by LDS-DMA, four
+// stages deep. Both operands are row-major in m, the reduction index, so
+// MFMA fragments are read with the LDS transpose load ds_read_b64_tr_b16:
+// within each group of 16 lanes, lane s addresses 4 consecutive elements of
+// row 8 g + (s >> 2) (+ 4 for the second half), columns c0 + 4 (s & 3), and
+// lane o receives column c0 + o of those rows. No transposed copy of either
+// input is made. Wave w owns j rows 16 (w & 3) .. + 15 and columns
+// 64 (w >> 2) .. + 63 (4 MFMA tiles, two waves per SIMD); the hi and lo
+// products go into the same fp32 accumulators. Q rows past M are clamped (P
+// is zero there), columns past C too (unstored).
+constexpr int GT_STAGES = 4;
+constexpr int GT_STAGE = 8192 + 4096 + 4096;  // elements: Q | P hi | P lo
+// 16-byte chunk swizzles that keep the transposed fragment reads free of
+// LDS bank conflicts (measured): 128 B rows (P) and 256 B rows (Q).
+__device__ __forceinline__ int gt_swz_p(int R) { return (((R >> 1) & 1) << 1) ^ (((R >> 3) & 1) << 2); }
+__device__ __forceinline__ int gt_swz_q(int R) { return ((R & 3) << 1) ^ (((R >> 3) & 1) << 3); }
+
+// s_waitcnt immediate: vmcnt <= vm (6 bits: [3:0] and [15:14]), lgkmcnt 0,
+// expcnt not waited on
+constexpr int waitcnt_vm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (0 << 8); }
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s_t;
+__device__ __forceinline__ uint2 tr_load(const uint16_t* p) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)p));
+}
+__device__ __forceinline__ bf16x8 frag(uint2 a, uint2 b) {
+  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+
+// One 64-row step on an LDS stage: all fragments are read first, then the
+// 16 MFMAs. The stage pointer is a restrict parameter: once inlined, its
+// loads carry alias-scope information telling the wait-count pass that they
+// do not read the stages being filled by the LDS-DMA in flight (otherwise it
+// forces vmcnt(0) before them; the kernel's own wait covers the stage read).
+__device__ __forceinline__ void gt_step(const uint16_t* __restrict__ st, const int (&aoff)[2][2],
+                                        const int (&boff)[2][2][4], f32x4 (&acc)[4]) {
+  uint2 ah[2][2], al[2][2], bq[2][4][2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ah[kk][h] = tr_load(st + aoff[kk][h]);
+      al[kk][h] = tr_load(st + 4096 + aoff[kk][h]);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) bq[kk][b][h] = tr_load(st + boff[kk][h][b]);
+    }
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const bf16x8 fh = frag(ah[kk][0], ah[kk][1]), fl = frag(al[kk][0], al[kk][1]);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const bf16x8 fb = frag(bq[kk][b][0], bq[kk][b][1]);
+      acc[b] = mfma16(fh, fb, acc[b]);
+      acc[b] = mfma16(fl, fb, acc[b]);
+    }
+  }
+}
+
 template <bool TRANS>
-__global__ __launch_bounds__(256) void grad_stream_kernel(const uint16_t* __restrict__ PtH,
-                                                           const uint16_t* __restrict__ PtL,
-                                                           const uint16_t* __restrict__ Q, int M,
-                                                           int Mp, int C, int rp, int mchunk,
-                                                           float* __restrict__ part) {
-  extern __shared__ __align__(16) uint16_t gsm[];  // GR_STAGES x (Q 8192 | H 4096 | L 4096)
+__global__ __launch_bounds__(512) void grad_tr_kernel(const uint16_t* __restrict__ Ph,
+                                                       const uint16_t* __restrict__ Pl,
+                                                       const uint16_t* __restrict__ Q, int M,
+                                                       int Mp, int C, int rp, int mchunk,
+                                                       float* __restrict__ part) {
+  extern __shared__ __align__(16) uint16_t gsm[];
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int jb = w & 3, ch = w >> 2;
   const int cbase = blockIdx.x * 128;
   const int s = blockIdx.y;
   const int jc = blockIdx.z;
   const int mbeg = s * mchunk;
   const int nsteps = max(0, min(Mp - mbeg, mchunk)) / 64;
-  constexpr int STAGE = 8192 + 4096 + 4096;
 
-  // Q: lane covers tile rows 16 w + 4 q + (l >> 4), 16-byte chunk l & 15
-  const uint32_t qcol = (uint32_t)min(cbase + 8 * (l & 15), C - 8) * 2u;
-  const int qrow = 16 * w + (l >> 4);
-  uint32_t poff[2];
+  // DMA lanes. Q: instruction q of wave w fills rows 8 w + 4 q .. + 3, lane i
+  // the physical chunk i & 15 of row 8 w + 4 q + (i >> 4). P: wave w fills
+  // rows 8 w .. + 7, lane i chunk i & 7 of row 8 w + (i >> 3).
+  int qrow[2];
+  uint32_t qcol[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const int row = 16 * w + 8 * q + (l >> 3);
-    poff[q] = (uint32_t)((jc * 64 + row) * Mp + mbeg + 8 * ((l & 7) ^ lds_swz(row))) * 2u;
+    qrow[q] = 8 * w + 4 * q + (l >> 4);
+    qcol[q] = (uint32_t)min(cbase + 8 * ((l & 15) ^ gt_swz_q(qrow[q])), C - 8) * 2u;
   }
+  const int prow = 8 * w + (l >> 3);
+  const uint32_t poff = (uint32_t)((mbeg + prow) * rp + jc * 64 + 8 * ((l & 7) ^ gt_swz_p(prow))) * 2u;
   auto issue = [&](int step) {
-    uint16_t* st = gsm + (step % GR_STAGES) * STAGE;
+    uint16_t* st = gsm + (step % GT_STAGES) * GT_STAGE;
     const int ms = min(step, nsteps - 1) * 64;
     const char* qb = reinterpret_cast<const char*>(Q);
-    const char* hb = reinterpret_cast<const char*>(PtH) + (size_t)ms * 2;
-    const char* lb = reinterpret_cast<const char*>(PtL) + (size_t)ms * 2;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = min(mbeg + ms + qrow + 4 * q, M - 1);  // rows past M: Pt is zero there
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(qb + ((uint32_t)row * (uint32_t)C * 2u + qcol)),
-                                       (lds_void_t*)(st + (16 * w + 4 * q) * 128), 16, 0, 0);
-    }
+    const char* hb = reinterpret_cast<const char*>(Ph) + (size_t)ms * rp * 2;
+    const char* lb = reinterpret_cast<const char*>(Pl) + (size_t)ms * rp * 2;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(hb + poff[q]), (lds_void_t*)(st + 8192 + (16 * w + 8 * q) * 64), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(lb + poff[q]), (lds_void_t*)(st + 12288 + (16 * w + 8 * q) * 64), 16, 0, 0);
+      const int row = min(mbeg + ms + qrow[q], M - 1);  // rows past M: P is zero there
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(qb + ((size_t)row * C * 2 + qcol[q])),
+                                       (lds_void_t*)(st + (8 * w + 4 * q) * 128), 16, 0, 0);
     }
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(hb + poff), (lds_void_t*)(st + 8192 + 8 * w * 64), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(lb + poff), (lds_void_t*)(st + 12288 + 8 * w * 64), 16, 0, 0);
   };
 
-  f32x4 acc[8];
+  // transposed-read addresses (elements, within a stage) for the two row
+  // halves h of a 32-row substep kk: lane (g = l >> 4, si = l & 15)
+  const int g = l >> 4, si = l & 15;
+  int aoff[2][2], boff[2][2][4];
 #pragma unroll
-  for (int cc = 0; cc < 8; ++cc) acc[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int sw = lds_swz(l & 15);  // swizzle of A-fragment row l & 15
-  const int g = l >> 4;
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int R = 32 * kk + 8 * g + 4 * h + (si >> 2);
+      const int ca = 16 * jb + 4 * (si & 3);
+      aoff[kk][h] = 8192 + R * 64 + 8 * ((ca >> 3) ^ gt_swz_p(R)) + (ca & 7);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int cb = 64 * ch + 16 * b + 4 * (si & 3);
+        boff[kk][h][b] = R * 128 + 8 * ((cb >> 3) ^ gt_swz_q(R)) + (cb & 7);
+      }
+    }
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (nsteps > 0) {
 #pragma unroll
-    for (int st = 0; st < GR_STAGES - 1; ++st) issue(st);
+    for (int st = 0; st < GT_STAGES - 1; ++st) issue(st);
     for (int step = 0; step < nsteps; ++step) {
-      // 8 DMA instructions per thread per stage, nothing else in flight
-      __builtin_amdgcn_s_waitcnt((8 * (GR_STAGES - 2)) | (7 << 4) | (0 << 8));
+      // 4 DMA instructions per thread per stage, nothing else in flight: the
+      // oldest stage has landed once at most (stages - 2) * 4 remain. LDS
+      // reads of the previous step are complete before any wave passes the
+      // barrier and refills their slot (a plain s_barrier: __syncthreads
+      // would also wait for the prefetches in flight).
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * (GT_STAGES - 2)));
       __builtin_amdgcn_s_barrier();
-      issue(step + GR_STAGES - 1);
-      const uint16_t* st = gsm + (step % GR_STAGES) * STAGE;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int ch = 8 * ((4 * kk + g) ^ sw);
-        const bf16x8 ah = lds_load8(reinterpret_cast<const __bf16*>(st + 8192 + (16 * w + (l & 15)) * 64 + ch));
-        const bf16x8 al = lds_load8(reinterpret_cast<const __bf16*>(st + 12288 + (16 * w + (l & 15)) * 64 + ch));
-        uint4 rq[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          rq[i] = *reinterpret_cast<const uint4*>(st + (32 * kk + 8 * g + i) * 128 + 8 * (l & 15));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          uint32_t lo4[4], hi4[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t x0 = (&rq[2 * i].x)[e], x1 = (&rq[2 * i + 1].x)[e];
-            lo4[i] = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
-            hi4[i] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
-          }
-          const bf16x8 b0 = __builtin_bit_cast(bf16x8, make_uint4(lo4[0], lo4[1], lo4[2], lo4[3]));
-          const bf16x8 b1 = __builtin_bit_cast(bf16x8, make_uint4(hi4[0], hi4[1], hi4[2], hi4[3]));
-          acc[2 * e] = mfma16(ah, b0, acc[2 * e]);
-          acc[2 * e] = mfma16(al, b0, acc[2 * e]);
-          acc[2 * e + 1] = mfma16(ah, b1, acc[2 * e + 1]);
-          acc[2 * e + 1] = mfma16(al, b1, acc[2 * e + 1]);
-        }
-      }
+      issue(step + GT_STAGES - 1);
+      gt_step(gsm + (step % GT_STAGES) * GT_STAGE, aoff, boff, acc);
     }
     __builtin_amdgcn_s_waitcnt(0);
   }
-  // stage the 64 x 128 partial through LDS, then write it coalesced
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(gsm);  // [64 j][129]
+  // D layout: lane holds j = 16 jb + 4 g + v, c = cbase + 64 ch + 16 b + si
+  const int j0 = jc * 64 + 16 * jb + 4 * g;
 #pragma unroll
-  for (int cc = 0; cc < 8; ++cc)
+  for (int b = 0; b < 4; ++b) {
+    const int c = cbase + 64 * ch + 16 * b + si;
+    if (c >= C) continue;
+    if (!TRANS) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[(16 * w + 4 * g + v) * 129 + 8 * (l & 15) + cc] = acc[cc][v];
-  __syncthreads();
-  if (!TRANS) {
-    // part[s][j][c]: thread -> j = tid >> 2, 32 columns
-    const int j = tid >> 2, c0 = 32 * (tid & 3);
-    float* dst = part + ((int64_t)s * rp + jc * 64 + j) * C + cbase + c0;
-    for (int c = 0; c < 32; ++c)
-      if (cbase + c0 + c < C) dst[c] = red[j * 129 + c0 + c];
-  } else {
-    // part[s][c][j]: thread -> c = tid >> 1, 32 j values
-    const int c = tid >> 1, j0 = 32 * (tid & 1);
-    if (cbase + c < C) {
-      float* dst = part + ((int64_t)s * C + cbase + c) * rp + jc * 64 + j0;
-      for (int j = 0; j < 32; ++j) dst[j] = red[(j0 + j) * 129 + c];
+      for (int v = 0; v < 4; ++v) part[((int64_t)s * rp + j0 + v) * C + c] = acc[b][v];
+    } else {
+      *reinterpret_cast<float4*>(part + ((int64_t)s * C + c) * rp + j0) =
+          make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
     }
   }
 }
@@ -510,11 +555,11 @@ hipError_t launch_proj(const uint16_t* L, const uint16_t* R, int M, int Kr, int 
   return hipGetLastError();
 }
 
-hipError_t launch_finalize(const float* part, int nsplit, int M, int r, int rp, float scale,
-                           float* P32, uint16_t* Ps, hipStream_t s) {
-  const int64_t total = (int64_t)M * rp;
+hipError_t launch_finalize(const float* part, int nsplit, int M, int Mp, int r, int rp, float scale,
+                           float* P32, uint16_t* Ph, uint16_t* Pl, hipStream_t s) {
+  const int64_t total = (int64_t)Mp * rp;
   hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part,
-                     nsplit, M, r, rp, scale, P32, Ps);
+                     nsplit, M, Mp, r, rp, scale, P32, Ph, Pl);
   return hipGetLastError();
 }
 
@@ -534,24 +579,23 @@ hipError_t launch_grad_reduce(const float* part, int nsplit, int r, int rp, int 
   return hipGetLastError();
 }
 
-hipError_t launch_split_t(const float* P, int M, int r, int rp, int Mp, uint16_t* hi, uint16_t* lo,
-                          hipStream_t s) {
-  const int64_t total = (int64_t)rp * Mp;
-  hipLaunchKernelGGL(split_t_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, P, M, r,
-                     rp, Mp, hi, lo);
+hipError_t launch_split_rows(const float* P, int M, int Mp, int r, int rp, float scale, uint16_t* hi,
+                             uint16_t* lo, hipStream_t s) {
+  const int64_t total = (int64_t)Mp * rp;
+  hipLaunchKernelGGL(split_rows_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, P, M, Mp, r,
+                     rp, scale, hi, lo);
   return hipGetLastError();
 }
 
-hipError_t launch_grad_stream(const uint16_t* PtH, const uint16_t* PtL, const uint16_t* Q, int M,
-                              int Mp, int C, int rp, int nsplit, bool trans, float* part,
-                              hipStream_t s) {
+hipError_t launch_grad_tr(const uint16_t* Ph, const uint16_t* Pl, const uint16_t* Q, int M, int Mp, int C,
+                          int rp, int nsplit, bool trans, float* part, hipStream_t s) {
   static bool configured = false;  // benign race: every thread sets the same value
-  const size_t smem = (size_t)GR_STAGES * (8192 + 4096 + 4096) * sizeof(uint16_t);
+  const size_t smem = (size_t)GT_STAGES * GT_STAGE * sizeof(uint16_t);
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&grad_stream_kernel<false>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&grad_tr_kernel<false>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&grad_stream_kernel<true>),
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&grad_tr_kernel<true>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     configured = true;
@@ -559,9 +603,9 @@ hipError_t launch_grad_stream(const uint16_t* PtH, const uint16_t* PtL, const ui
   const int mchunk = ((Mp + nsplit - 1) / nsplit + 63) / 64 * 64;
   dim3 grid((C + 127) / 128, nsplit, rp / 64);
   if (trans)
-    hipLaunchKernelGGL(grad_stream_kernel<true>, grid, dim3(256), smem, s, PtH, PtL, Q, M, Mp, C, rp, mchunk, part);
+    hipLaunchKernelGGL(grad_tr_kernel<true>, grid, dim3(512), smem, s, Ph, Pl, Q, M, Mp, C, rp, mchunk, part);
   else
-    hipLaunchKernelGGL(grad_stream_kernel<false>, grid, dim3(256), smem, s, PtH, PtL, Q, M, Mp, C, rp, mchunk, part);
+    hipLaunchKernelGGL(grad_tr_kernel<false>, grid, dim3(512), smem, s, Ph, Pl, Q, M, Mp, C, rp, mchunk, part);
   return hipGetLastError();
 }
 
