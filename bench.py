@@ -16,7 +16,13 @@ Legs timed in the same run (HBM-bound rows of the path):
             LoRA r=64, rotating over >= 1 GB of distinct weight sets
   gemm512   forward at M = 512 (small-GEMM regime)
   roofline  the dominant kernel (dequant-in-LDS MFMA GEMM, forward
-            orientation) over the seven layer shapes, timed with HIP events
+            orientation) over the seven layer shapes, timed with HIP events;
+            its HBM traffic per launch comes from the FETCH_SIZE / WRITE_SIZE
+            counter runs recorded in profiles/ (null when the GEMM source
+            has changed since)
+  copycal   one elementwise pass reading and writing exactly 1 GiB each, the
+            calibration point of those counters
+            (see bit_nf4_quantized_12_amd/pmc_traffic.py)
 cpu_baseline: the float64 oracle (tests only, never on the product path) on
 a bounded sample of the step's work, on the host cores.
 """
@@ -32,6 +38,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "roofline_gemm_traffic_llama7b.json")
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 Q_BYTES_PER_W = 2.0 + 0.5 + 1.0 / 64 + 4.0 / 16384   # read bf16, write codes, c2, c1
 
@@ -152,8 +159,9 @@ def main():
         flops_per_launch = sum(2.0 * M * L["N"] * L["K"] for L in lin) / len(lin)
         achieved = flops_per_launch / avg_s / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                    "kernel": "gemm_kernel<false,false> (qlora_nf4_matmul, X W~^T)",
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": measured_traffic(),
+                    "kernel": "gemm_kernel<false, false, true> (qlora_nf4_matmul, X W~^T)",
                     "avg_launch_us": round(avg_s * 1e6, 2), "launches": launches,
                     "flops_per_launch": flops_per_launch}
         log(f"roofline kernel: avg {avg_s * 1e6:.1f} us/launch, {achieved:.1f} TFLOP/s")
@@ -169,6 +177,14 @@ def main():
         legs["gemm_dx_orientation"] = {"tflops": round(flops_per_launch * launches / tt / 1e12, 2),
                                        "avg_launch_us": round(tt / launches * 1e6, 2)}
         del outs, outs_t
+
+    if "copycal" in want:
+        # one elementwise pass of exactly 1 GiB in and 1 GiB out (bf16 negation)
+        src = torch.zeros(1 << 29, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- few-token forward (GEMV) and M = 512 ----------------------------------------------
     if "gemv" in want or "gemm512" in want:
@@ -283,6 +299,19 @@ def main():
         "legs": legs,
     }
     print(json.dumps(line), flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per launch of the roofline kernel, if measured on the current GEMM source."""
+    try:
+        from bit_nf4_quantized_12_amd import pmc_traffic
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+        if rec.get("gemm_source_sha256") != pmc_traffic.gemm_source_sha():
+            return None
+        return round(rec["traffic_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        return None
 
 
 def cpu_baseline(target_s, log):
