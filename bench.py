@@ -13,7 +13,9 @@ Legs timed in the same run (HBM-bound rows of the path):
             3 x 22016x8192 weights per layer), 2.51587 B moved per weight
   dequant   round trip of the same stack to bf16, 2.51587 B per weight
   gemv      few-token forward (M = 1, 16) of 4096x4096 and 11008x4096 with
-            LoRA r=64, rotating over >= 1 GB of distinct weight sets
+            LoRA r=64, rotating over >= 1 GB of distinct weight sets; the
+            chain of calls is captured once as a HIP graph and replayed (the
+            eager time per call, host launch cost included, is reported too)
   gemm512   forward at M = 512 (small-GEMM regime)
   roofline  the dominant kernel (dequant-in-LDS MFMA GEMM, forward
             orientation) over the seven layer shapes, timed with HIP events;
@@ -211,15 +213,24 @@ def main():
 
                 run_all()
                 reps = 5
-                t = timed(run_all, reps)
-                per = t / (reps * nsets)
+                t_eager = timed(run_all, reps) / (reps * nsets)
+                # the same chain of calls captured once as a HIP graph and replayed:
+                # time per call without the host's launch cost
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph):
+                    run_all()
+                graph.replay()
+                per = timed(graph.replay, reps) / (reps * nsets)
+                del graph
                 byts = wbytes + 2.0 * r * (K + N) + 2.0 * Mg * (K + N)
                 fl = 2.0 * Mg * N * K + 2.0 * Mg * r * (K + N)
                 key = f"{'gemv' if Mg <= 16 else 'gemm'}_M{Mg}_{N}x{K}"
                 legs[key] = {"us_per_call": round(per * 1e6, 2), "GB/s": round(byts / per / 1e9, 1),
                              "hbm_frac": round(byts / per / 1e9 / PEAK_HBM_GBS, 4),
-                             "TFLOP/s": round(fl / per / 1e12, 2), "weight_sets": nsets}
-                log(f"{key}: {per * 1e6:.2f} us/call, {byts / per / 1e9:.0f} GB/s")
+                             "TFLOP/s": round(fl / per / 1e12, 2), "weight_sets": nsets,
+                             "timing": "hip graph of the chain of calls",
+                             "us_per_call_eager": round(t_eager * 1e6, 2)}
+                log(f"{key}: {per * 1e6:.2f} us/call ({t_eager * 1e6:.2f} eager), {byts / per / 1e9:.0f} GB/s")
             del sets
             torch.cuda.empty_cache()
 

@@ -100,6 +100,21 @@ __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
     }
   };
 
+  // With r <= 64 the epilogue operands are fetched before the weight stream
+  // so their latency overlaps it: thread t holds B element t (rows n0 ..
+  // n0 + 15, r columns) and the first 16 split-K partials of T element t
+  // (t < M r); a longer split is summed after the main loop. Larger ranks
+  // fetch them after the main loop.
+  const bool pre = r <= 64;
+  const int nb = 16 * r, nt = M * r;
+  const bool hasb = pre && tid < nb, hast = pre && tid < nt;
+  const int br = hasb ? tid / r : 0, bj = hasb ? tid % r : 0;
+  const uint16_t bval = hasb ? B[(int64_t)min(n0 + br, N - 1) * r + bj] : (uint16_t)0;
+  const int tm = hast ? tid / r : 0, tj = hast ? tid % r : 0;
+  float tp[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) tp[k] = (hast && k < tsplit) ? tpart[((int64_t)k * M + tm) * rp + tj] : 0.0f;
+
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int ch = w; ch < nchunks; ch += 2 * GV_WAVES) {
     uint4 cw0, cw1;
@@ -114,18 +129,31 @@ __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
 #pragma unroll
   for (int v = 0; v < 4; ++v) red[w][4 * g + v][c] = acc[v];
 
-  // B rows n0 .. n0 + 15 (r columns each) into LDS
-  for (int idx = tid; idx < 16 * r; idx += 64 * GV_WAVES) {
-    const int rr = idx / r, j = idx % r;
-    sB[rr * r + j] = B[(int64_t)min(n0 + rr, N - 1) * r + j];
-  }
-  // T = sum of the split-K partials of X A^T, rows < M, columns < r
-  for (int idx = tid; idx < M * r; idx += 64 * GV_WAVES) {
-    const int m = idx / r, j = idx % r;
-    float s = 0.0f;
-    for (int k = 0; k < tsplit; ++k) s += tpart[((int64_t)k * M + m) * rp + j];
-    sT[m][j] = s;
-    if (blockIdx.x == 0 && T_out) T_out[(int64_t)m * r + j] = s;
+  // B rows n0 .. n0 + 15 (r columns each) and T = sum of the split-K
+  // partials of X A^T (rows < M, columns < r) into LDS
+  if (pre) {
+    // 16 r <= 1024 and M r <= 1024 threads (M <= 16)
+    if (hasb) sB[br * r + bj] = bval;
+    if (hast) {
+      float s = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) s += tp[k];
+      for (int k = 16; k < tsplit; ++k) s += tpart[((int64_t)k * M + tm) * rp + tj];
+      sT[tm][tj] = s;
+      if (blockIdx.x == 0 && T_out) T_out[(int64_t)tm * r + tj] = s;
+    }
+  } else {
+    for (int idx = tid; idx < 16 * r; idx += 64 * GV_WAVES) {
+      const int rr = idx / r, j = idx % r;
+      sB[rr * r + j] = B[(int64_t)min(n0 + rr, N - 1) * r + j];
+    }
+    for (int idx = tid; idx < M * r; idx += 64 * GV_WAVES) {
+      const int m = idx / r, j = idx % r;
+      float s = 0.0f;
+      for (int k = 0; k < tsplit; ++k) s += tpart[((int64_t)k * M + m) * rp + j];
+      sT[m][j] = s;
+      if (blockIdx.x == 0 && T_out) T_out[(int64_t)m * r + j] = s;
+    }
   }
   __syncthreads();
   // thread -> (m, row): m = tid >> 4, row = tid & 15 (first 256 threads)

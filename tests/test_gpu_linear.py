@@ -66,7 +66,7 @@ def test_single_linear_256_r8():
 @pytest.mark.parametrize("M,N,K,r", [
     (1, 100, 64, 1), (3, 257, 192, 5), (16, 300, 320, 8), (17, 129, 128, 16),
     (130, 200, 384, 33), (256, 512, 512, 64), (70, 1000, 640, 64), (129, 131, 64, 256),
-    (200, 96, 1024, 2),
+    (200, 96, 1024, 2), (8, 136, 256, 100), (16, 72, 128, 256),
 ])
 def test_ragged_shapes(M, N, K, r):
     run_case(M, N, K, r, 16.0, cfg=101)
