@@ -290,17 +290,20 @@ def linear_fwd(X, W, A, B, s):
     return Y, T
 
 
-def linear_bwd(X, W, A, B, dY, s):
+def linear_bwd(X, W, A, B, dY, s, need_dX=True):
     """Input and adapter gradients of linear_fwd for the upstream gradient dY.
 
     U = dY B; dX = dY W + s U A; dA = s U^T X; dB = s dY^T T with T = X A^T.
-    Returns (dX, dA, dB), float64.
+    Returns (dX, dA, dB), float64; dX is None when need_dX is false (W is
+    then not used and may be None).
     """
-    X, W, A, B, dY = (np.asarray(t, dtype=np.float64) for t in (X, W, A, B, dY))
+    X, A, B, dY = (np.asarray(t, dtype=np.float64) for t in (X, A, B, dY))
     s = float(s)
     T = X @ A.T
     U = dY @ B
-    dX = dY @ W + s * (U @ A)
+    dX = None
+    if need_dX:
+        dX = dY @ np.asarray(W, dtype=np.float64) + s * (U @ A)
     dA = s * (U.T @ X)
     dB = s * (dY.T @ T)
     return dX, dA, dB

@@ -14,19 +14,29 @@ import torch
 import bit_nf4_quantized_12_amd as q
 import oracle
 from bit_nf4_quantized_12_amd import synth
+from tests import oracle_pool
 from tests.parity import assert_close, bf16_bits_to_f32, report
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def _oracle_weight(w32):
-    pk, c2, c1 = oracle.quantize_nf4_dq(w32)
+def _oracle_weight(w32, pool=None):
+    if pool is not None:
+        pk, c2, c1 = oracle_pool.quantize_parallel(w32, pool)
+    else:
+        pk, c2, c1 = oracle.quantize_nf4_dq(w32)
     return oracle.bf16_round(oracle.dequant(pk, c2, c1, w32.size)).reshape(w32.shape)
 
 
+@pytest.fixture(scope="module")
+def pool():
+    with oracle_pool.make_pool() as p:
+        yield p
+
+
 def run_case(M, N, K, r, alpha, seed=0, cfg=100, rows=None, w_dist="normal", backward=True,
-             save_T=True):
+             save_T=True, pool=None):
     report(f"linear parity: M={M} N={N} K={K} r={r} alpha={alpha} save_T={save_T}")
     case = synth.linear_case(M, N, K, r, seed=seed, cfg=cfg, w_dist=w_dist)
     s = alpha / r
@@ -43,7 +53,7 @@ def run_case(M, N, K, r, alpha, seed=0, cfg=100, rows=None, w_dist="normal", bac
     if T is not None:
         got["T"] = T.cpu().numpy()
 
-    Wo = _oracle_weight(w32)
+    Wo = _oracle_weight(w32, pool)
     sel = np.arange(M) if rows is None else np.asarray(rows)
     Yr, Tr = oracle.linear_fwd(x[sel], Wo, a, b, s)
     assert_close(got["Y"][sel], Yr, "Y")
@@ -52,7 +62,7 @@ def run_case(M, N, K, r, alpha, seed=0, cfg=100, rows=None, w_dist="normal", bac
     if backward:
         dXr, _, _ = oracle.linear_bwd(x[sel], Wo, a, b, dy[sel], s)
         assert_close(got["dX"][sel], dXr, "dX")
-        _, dAr, dBr = oracle.linear_bwd(x, Wo, a, b, dy, s)
+        _, dAr, dBr = oracle.linear_bwd(x, None, a, b, dy, s, need_dX=False)
         assert_close(got["dA"], dAr, "dA")
         assert_close(got["dB"], dBr, "dB")
     return got
@@ -113,6 +123,14 @@ def test_llama7b_projections_forward(M, N):
 
 
 @pytest.mark.parametrize("N,K", [(4096, 4096), (11008, 4096), (4096, 11008)])
-def test_llama7b_layer_linears_8192_tokens(N, K):
+def test_llama7b_layer_linears_8192_tokens(N, K, pool):
     rows = np.random.default_rng(N + K).choice(8192, 96, replace=False)
-    run_case(8192, N, K, 64, 16.0, cfg=3, rows=rows)
+    run_case(8192, N, K, 64, 16.0, cfg=3, rows=rows, pool=pool)
+
+
+@pytest.mark.parametrize("N,K", [(8192, 8192), (22016, 8192), (8192, 22016)])
+def test_65b_layer_linears_8192_tokens(N, K, pool):
+    # 65B-class layer shapes, weights 0.02 * Student-t(5) (heavy tails stress
+    # the block absmax); Y and dX on 256 seeded rows, dA and dB in full
+    rows = np.random.default_rng(N + 3 * K).choice(8192, 256, replace=False)
+    run_case(8192, N, K, 64, 16.0, cfg=4, rows=rows, w_dist="student_t", pool=pool)

@@ -11,6 +11,7 @@ import torch
 import bit_nf4_quantized_12_amd as q
 import oracle
 from bit_nf4_quantized_12_amd import synth
+from tests import oracle_pool
 from tests.parity import report
 
 pytestmark = pytest.mark.gpu
@@ -100,3 +101,49 @@ def test_deterministic_and_idempotent():
     W16 = torch.from_numpy(a[4].view(np.int16)).view(torch.bfloat16)
     codes2 = _gpu_quant(W16)[0]
     np.testing.assert_array_equal(codes2, a[0])
+
+
+def test_65b_class_stack_bit_exact_sampled():
+    """80 layers x (4 x 8192^2 + 3 x 22016x8192) = 64.76e9 weights ~ N(0, 0.02),
+    generated on the GPU (seeded) and quantised there one tensor at a time.
+    Layers 0 and 79 are compared in full; every other layer on 64 seeded
+    random groups of 16384 weights spread over its seven tensors. Each group
+    is quantised independently, so the oracle runs on the copied-back groups
+    alone."""
+    per_layer = [(8192, 8192)] * 4 + [(22016, 8192)] * 3
+    G = oracle_pool.GROUP
+    rng = np.random.default_rng(5)
+    with oracle_pool.make_pool() as pool:
+        for li in range(80):
+            full = li in (0, 79)
+            report(f"65B-class stack: layer {li} ({'full' if full else 'sampled groups'})")
+            samples = []  # (label, weights, codes, c2, c1) of sampled groups
+            for j, (N, K) in enumerate(per_layer):
+                n = N * K
+                ng = n // G
+                w = synth.device_normal_bf16(n, 0.02, 1_000_000 + 10 * li + j, DEV)
+                codes, c2, c1 = q.qlora_quantize_nf4_dq(w)
+                if full:
+                    wh = w.float().cpu().numpy()
+                    pk, oc2, oc1 = oracle_pool.quantize_parallel(wh, pool)
+                    lab = f"layer {li} tensor {j}"
+                    np.testing.assert_array_equal(codes.cpu().numpy(), pk, err_msg=f"{lab}: codes")
+                    np.testing.assert_array_equal(c2.cpu().numpy(), oc2, err_msg=f"{lab}: c2")
+                    np.testing.assert_array_equal(c1.cpu().numpy().view(np.uint32), oc1.view(np.uint32),
+                                                  err_msg=f"{lab}: c1")
+                else:
+                    k = 10 if j < 6 else 4  # 6 x 10 + 4 = 64 groups per layer
+                    gs = torch.from_numpy(np.sort(rng.choice(ng, k, replace=False))).to(DEV)
+                    wg = w.view(ng, G)[gs].float().cpu().numpy()
+                    cg = codes.view(ng, G // 2)[gs].cpu().numpy()
+                    c2g = c2.view(ng, 256)[gs].cpu().numpy()
+                    c1g = c1[gs].cpu().numpy()
+                    for t in range(k):
+                        samples.append((f"layer {li} tensor {j} group {int(gs[t])}", wg[t], cg[t], c2g[t], c1g[t]))
+                del w, codes, c2, c1
+            if samples:
+                want = oracle_pool.quantize_slices(pool, [smp[1] for smp in samples])
+                for (lab, _, cg, c2g, c1g), (pk, oc2, oc1) in zip(samples, want):
+                    np.testing.assert_array_equal(cg, pk, err_msg=f"{lab}: codes")
+                    np.testing.assert_array_equal(c2g, oc2, err_msg=f"{lab}: c2")
+                    assert c1g.view(np.uint32) == oc1.view(np.uint32)[0], f"{lab}: c1"
