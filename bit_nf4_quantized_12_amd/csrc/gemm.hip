@@ -8,20 +8,23 @@
 // LoRA side follows "QLoRA: Efficient Fine-Tuning of Quantized Language
 // Models" (mbrenndoerfer.com), section "Low-Rank Adaptation (LoRA)".
 //
-// Tile 256 x 256 outputs, 64-deep reduction steps (one NF4 block), 8 wave64
-// in 2 x 4, each wave 128 x 64 outputs = 8 x 4 v_mfma_f32_16x16x32_bf16
-// tiles (128 float32 accumulators per lane), two waves per SIMD: while one
-// wave keeps the matrix core busy the other issues its unpacking VALU work.
-// LDS holds two stages of the activation tile and of the weight tile (bf16,
-// 128 KB in all, 16-byte chunks XOR-swizzled per row so MFMA operand reads
-// are conflict free). The activation tile is streamed global -> LDS by
-// LDS-DMA (global_load_lds_dwordx4); no registers involved.
+// Tile BM x BN outputs (256 x 256, or 512 x 128 for large M), 64-deep
+// reduction steps (one NF4 block), 8 wave64 in (BM / 128) x (BN / 64), each
+// wave 128 x 64 outputs = 8 x 4 v_mfma_f32_16x16x32_bf16 tiles (128 float32
+// accumulators per lane), two waves per SIMD: while one wave keeps the matrix
+// core busy the other issues its unpacking VALU work. The unpack work per
+// step grows with BN and the MFMA work with BM x BN, so the 512 x 128 tile
+// halves the unpacking per MFMA at the same LDS read volume per step. LDS
+// holds two stages of the activation tile and of the weight tile (bf16,
+// 128 or 160 KB in all, 16-byte chunks XOR-swizzled per row so MFMA operand
+// reads are conflict free). The activation tile is streamed global -> LDS
+// by LDS-DMA (global_load_lds_dwordx4); no registers involved.
 //
-// Weight tiles are unpacked in registers: each thread owns half a block (32
-// codes) per step, builds the block's 16-entry table of bf16(q[c] * c^)
-// (16 multiplies, 8 conversions, 8 byte shuffles) and maps every code
-// through it with v_perm byte selects -- no LDS lookups, exact W~. Codes are
-// fetched two steps ahead, activations one step ahead.
+// Weight tiles are unpacked in registers: each thread owns BN / 8 codes of
+// one block per step (half or a quarter of it), builds the block's 16-entry
+// table of bf16(q[c] * c^) (16 multiplies, 8 conversions, 8 byte shuffles)
+// and maps every code through it with v_perm byte selects -- no LDS lookups,
+// exact W~. Codes are fetched two steps ahead, activations one step ahead.
 //
 // Workgroups are ordered so that each XCD (workgroup id mod 8) owns a
 // contiguous band of output tiles: the activation rows and weight columns
@@ -31,7 +34,7 @@
 namespace qlora {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64, NT = 512;
+constexpr int BK = 64, NT = 512;
 
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
@@ -104,45 +107,49 @@ __device__ __forceinline__ uint4 load_row8(const uint16_t* __restrict__ base, in
 __device__ __forceinline__ int swz(int R) { return lds_swz(R); }
 __device__ __forceinline__ int tile_off(int R, int c) { return R * 64 + 8 * (c ^ swz(R)); }
 
-// Half a weight block (32 codes) and its block constant.
-struct WHalf {
-  uint4 c;
+// The QW code words (8 QW codes of one block) a thread unpacks in a step,
+// and their block constant.
+template <int QW>
+struct WPart {
+  uint32_t c[QW];
   float chat;
 };
 
-// Thread -> weight half-block of a step. Forward: thread t owns tile row
-// t >> 1 (weight row n0 + t/2), half t & 1 of the step's block. Input
-// gradient: lane l owns weight row k0 + l, wave w the block (w >> 1) of the
-// tile's four 64-column blocks, half w & 1.
-template <bool TW>
+// Thread -> weight codes of a step (QW words = 8 QW codes; TPR = 8 / QW
+// threads share a block). Forward: thread t owns tile row t / TPR (weight
+// row n0 + t / TPR), part t % TPR of the step's block. Input gradient: lane
+// l owns weight row k0 + l, wave w the weight columns n0 + 8 QW w ..
+template <bool TW, int QW>
 __device__ __forceinline__ void wlane(int tid, int n0, int64_t& row, int64_t& col) {
+  constexpr int TPR = 8 / QW;
   const int w = tid >> 6, l = tid & 63;
   if (!TW) {
-    row = n0 + (tid >> 1);
-    col = 32 * (tid & 1);
+    row = n0 + tid / TPR;
+    col = 8 * QW * (tid % TPR);
   } else {
     row = l;
-    col = n0 + 64 * (w >> 1) + 32 * (w & 1);
+    col = n0 + 8 * QW * w;
   }
 }
 
-// Unpack word q (weights 8q .. 8q+7 of this thread's half block) into the
+// Unpack word q (weights 8q .. 8q+7 of this thread's codes) into the
 // weight tile of an LDS stage.
-template <bool TW>
+template <bool TW, int QW>
 __device__ __forceinline__ void store_wword(uint32_t word, int q, const BlockTable& t,
                                             uint16_t* __restrict__ dst, int tid) {
+  constexpr int TPR = 8 / QW;
   if (!TW) {
-    // tile row tid >> 1, reduction chunk 4 (tid & 1) + q
+    // tile row tid / TPR, reduction chunk QW (tid % TPR) + q
     uint32_t o[4];
     lookup8(word, t, o);
-    *reinterpret_cast<uint4*>(dst + tile_off(tid >> 1, 4 * (tid & 1) + q)) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(dst + tile_off(tid / TPR, QW * (tid % TPR) + q)) = make_uint4(o[0], o[1], o[2], o[3]);
   } else {
-    // element e of the word is W~[k0 + l][n0 + 32 w + 8 q + e]: tile row
-    // 32 w + 8 q + e, reduction position l
+    // element e of the word is W~[k0 + l][n0 + 8 QW w + 8 q + e]: tile row
+    // 8 QW w + 8 q + e, reduction position l
     const int w = tid >> 6, l = tid & 63;
     uint32_t E[2], O[2];
     lookup8_split(word, t, E, O);
-    const int r0 = 32 * w + 8 * q;
+    const int r0 = 8 * QW * w + 8 * q;
     const uint16_t v[8] = {(uint16_t)E[0], (uint16_t)O[0], (uint16_t)(E[0] >> 16), (uint16_t)(O[0] >> 16),
                            (uint16_t)E[1], (uint16_t)O[1], (uint16_t)(E[1] >> 16), (uint16_t)(O[1] >> 16)};
 #pragma unroll
@@ -150,19 +157,34 @@ __device__ __forceinline__ void store_wword(uint32_t word, int q, const BlockTab
   }
 }
 
-template <bool TW>
-__device__ __forceinline__ void store_whalf(const WHalf& h, const Levels& lv, uint16_t* __restrict__ dst, int tid) {
+template <bool TW, int QW>
+__device__ __forceinline__ void store_wpart(const WPart<QW>& h, const Levels& lv, uint16_t* __restrict__ dst, int tid) {
   const BlockTable t = make_table(h.chat, lv);
-  const uint32_t words[4] = {h.c.x, h.c.y, h.c.z, h.c.w};
 #pragma unroll
-  for (int q = 0; q < 4; ++q) store_wword<TW>(words[q], q, t, dst, tid);
+  for (int q = 0; q < QW; ++q) store_wword<TW, QW>(h.c[q], q, t, dst, tid);
+}
+
+// QW code words at codes + (e >> 1) (e a multiple of 8 QW).
+template <int QW>
+__device__ __forceinline__ void load_words(const uint8_t* __restrict__ codes, int64_t e, uint32_t (&c)[QW]) {
+  if (QW == 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(codes + (e >> 1));
+    c[0] = v.x; c[1] = v.y; c[2] = v.z; c[3] = v.w;
+  } else {
+    const uint2 v = *reinterpret_cast<const uint2*>(codes + (e >> 1));
+    c[0] = v.x; c[1] = v.y;
+  }
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gbl_void_t;
 
-template <bool TW, bool LORA, bool VEC>
+template <int BM, int BN, bool TW, bool LORA, bool VEC>
 __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
+  constexpr int WN = BN / 64;        // waves along the output columns
+  constexpr int QW = BN / 64;        // code words unpacked per thread per step
+  constexpr int XJ = BM / 64;        // activation LDS-DMA instructions per wave per step
+  static_assert((BM / 128) * WN == NT / 64, "8 waves of 128 x 64");
   extern __shared__ __align__(16) uint16_t smem[];
   uint16_t* sA = smem;                // [2][BM * 64] activation tiles
   uint16_t* sB = smem + 2 * BM * 64;  // [2][BN * 64] weight tiles
@@ -170,7 +192,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
   const int tid = threadIdx.x;
   const int l = tid & 63;
   const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
-  const int wm = wu >> 2, wn = wu & 3;
+  const int wm = wu / WN, wn = wu % WN;
 
   // XCD-aware tile order: workgroup g runs on XCD g % 8; XCD x owns the
   // contiguous tile range [x * per, (x + 1) * per) in row-major tile order.
@@ -186,15 +208,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
 
   // ---- activation tile of step kt -> stage st --------------------------------------
   // VEC (Kred % 64 == 0): LDS-DMA, 16 B per lane; instruction j of wave w
-  // fills rows 32 w + 8 j .. +7 (1 KB), lane i the physical chunk i & 7 of
-  // row 32 w + 8 j + (i >> 3), i.e. the logical chunk (i & 7) ^ swz(row).
-  // Rows past the end are clamped (they only feed unstored outputs); steps
-  // past the end reload the last step (prefetch overrun, never used). Lane
-  // byte offsets are fixed; the step moves a uniform base.
-  uint32_t xoff[4];
+  // fills rows (BM / 8) w + 8 j .. +7 (1 KB), lane i the physical chunk i & 7
+  // of row (BM / 8) w + 8 j + (i >> 3), i.e. the logical chunk
+  // (i & 7) ^ swz(row). Rows past the end are clamped (they only feed
+  // unstored outputs); steps past the end reload the last step (prefetch
+  // overrun, never used). Lane byte offsets are fixed; the step moves a
+  // uniform base.
+  uint32_t xoff[XJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int R = 32 * wu + 8 * j + (l >> 3);
+  for (int j = 0; j < XJ; ++j) {
+    const int R = (BM / 8) * wu + 8 * j + (l >> 3);
     const int row = min(m0 + R, p.M - 1);
     xoff[j] = (uint32_t)(row * p.Kred + 8 * ((l & 7) ^ swz(R))) * 2u;
   }
@@ -203,13 +226,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
       const int ke = min(kt, nk - 1);
       const char* base = reinterpret_cast<const char*>(p.act) + (size_t)ke * (BK * 2);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < XJ; ++j)
         __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + xoff[j]),
-                                         (lds_void_t*)(sA + st * BM * 64 + (32 * wu + 8 * j) * 64), 16, 0, 0);
+                                         (lds_void_t*)(sA + st * BM * 64 + ((BM / 8) * wu + 8 * j) * 64), 16, 0, 0);
     } else {
       const int k0 = kt * BK;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < BM / 64; ++c) {
         const int id = tid + NT * c;
         const uint4 v = load_row8(p.act, p.Kred, m0 + (id >> 3), p.M, k0 + 8 * (id & 7), p.Kred, false);
         *reinterpret_cast<uint4*>(&sA[st * BM * 64 + tile_off(id >> 3, id & 7)]) = v;
@@ -217,32 +240,32 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
     }
   };
 
-  // ---- weight half-block of step kt -------------------------------------------------
+  // ---- weight codes of step kt ------------------------------------------------------
   int64_t wrow, wcol;
-  wlane<TW>(tid, n0, wrow, wcol);
+  wlane<TW, QW>(tid, n0, wrow, wcol);
   const int64_t wstep = TW ? (int64_t)BK * p.wK : (int64_t)BK;  // elements per step
   // VEC: every step is a full 64 reduction rows (forward: columns), so only
   // the output side can run past the end: clamp it (unstored outputs).
-  const int64_t wbase = TW ? wrow * p.wK + min(wcol, p.wK - 32)
+  const int64_t wbase = TW ? wrow * p.wK + min(wcol, p.wK - 8 * QW)
                            : min(wrow, p.wN - 1) * p.wK + wcol;
-  auto load_w = [&](int kt) -> WHalf {
-    WHalf h;
+  auto load_w = [&](int kt) -> WPart<QW> {
+    WPart<QW> h;
     if (VEC) {
       const int ke = min(kt, nk - 1);
       const int64_t e = (int64_t)ke * wstep + wbase;
-      h.c = *reinterpret_cast<const uint4*>(p.codes + (e >> 1));
+      load_words<QW>(p.codes, e, h.c);
       h.chat = block_scale(p.c2, p.c1, e >> 6);
     } else {
-      // general reduction length: a half block past the reduction end gets
-      // c^ = 0 (its unpacked weights are exact zeros, which zero the
-      // reduction tail); other out-of-range reads are clamped.
+      // general reduction length: codes past the reduction end get c^ = 0
+      // (their unpacked weights are exact zeros, which zero the reduction
+      // tail); other out-of-range reads are clamped.
       int64_t n = TW ? (int64_t)kt * BK + wrow : wrow;
       int64_t col = TW ? wcol : (int64_t)kt * BK + wcol;
       const bool ok = n < p.wN && col < p.wK;
       n = min(n, p.wN - 1);
-      col = min(col, p.wK - 32);
+      col = min(col, p.wK - 8 * QW);
       const int64_t e = n * p.wK + col;
-      h.c = *reinterpret_cast<const uint4*>(p.codes + (e >> 1));
+      load_words<QW>(p.codes, e, h.c);
       const float chat = block_scale(p.c2, p.c1, e >> 6);
       h.chat = ok ? chat : 0.0f;
     }
@@ -257,8 +280,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
 
   // prologue: stage 0 complete, codes of step 1 in flight
   load_x(0, 0);
-  WHalf wnext = load_w(0);
-  store_whalf<TW>(wnext, p.lv, sB, tid);
+  WPart<QW> wnext = load_w(0);
+  store_wpart<TW, QW>(wnext, p.lv, sB, tid);
   wnext = load_w(1);
   __builtin_amdgcn_s_waitcnt(0);  // stage 0 LDS-DMA landed (vmcnt = lgkmcnt = 0)
   __syncthreads();
@@ -273,7 +296,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
     load_x(kt + 1, st ^ 1);
-    const WHalf wcur = wnext;
+    const WPart<QW> wcur = wnext;
     wnext = load_w(kt + 2);
 
     const uint16_t* a_s = sA + st * BM * 64;
@@ -293,7 +316,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
     }
     // unpack the next weight tile into the other stage (free since the last
     // barrier); steps past the end unpack a clamped block into an unused stage
-    store_whalf<TW>(wcur, p.lv, sB + (st ^ 1) * BN * 64, tid);
+    store_wpart<TW, QW>(wcur, p.lv, sB + (st ^ 1) * BN * 64, tid);
     __builtin_amdgcn_s_waitcnt(0);  // this step's LDS-DMA and LDS writes are complete
     __syncthreads();
   }
@@ -304,14 +327,20 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
     // LDS-DMA like the main loop; the loop ended on a barrier.
     for (int kr = 0; kr < p.rp; kr += BK) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int R = 32 * wu + 8 * j + (l >> 3);
+      for (int j = 0; j < BM / 64; ++j) {
+        const int R = (BM / 8) * wu + 8 * j + (l >> 3);
         const int c = (l & 7) ^ swz(R);
-        const int ra = min(m0 + R, p.M - 1), rb = min(n0 + R, p.Nout - 1);
+        const int ra = min(m0 + R, p.M - 1);
         __builtin_amdgcn_global_load_lds((gbl_void_t*)(p.lora_l + (int64_t)ra * p.rp + kr + 8 * c),
-                                         (lds_void_t*)(sA + (32 * wu + 8 * j) * 64), 16, 0, 0);
+                                         (lds_void_t*)(sA + ((BM / 8) * wu + 8 * j) * 64), 16, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < BN / 64; ++j) {
+        const int R = (BN / 8) * wu + 8 * j + (l >> 3);
+        const int c = (l & 7) ^ swz(R);
+        const int rb = min(n0 + R, p.Nout - 1);
         __builtin_amdgcn_global_load_lds((gbl_void_t*)(p.lora_r + (int64_t)rb * p.rp + kr + 8 * c),
-                                         (lds_void_t*)(sB + (32 * wu + 8 * j) * 64), 16, 0, 0);
+                                         (lds_void_t*)(sB + ((BN / 8) * wu + 8 * j) * 64), 16, 0, 0);
       }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -350,27 +379,30 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
     }
 }
 
-constexpr size_t kSmemBytes = 2 * (BM + BN) * 64 * sizeof(uint16_t);
-
-template <bool TW, bool LORA, bool VEC>
+template <int BM, int BN, bool TW, bool LORA, bool VEC>
 hipError_t launch_variant(const GemmParams& p, hipStream_t s) {
+  constexpr size_t smem_bytes = 2 * (BM + BN) * 64 * sizeof(uint16_t);
   static bool configured = false;  // benign race: every thread sets the same value
   if (!configured) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<TW, LORA, VEC>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmemBytes);
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<BM, BN, TW, LORA, VEC>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_bytes);
     if (e != hipSuccess) return e;
     configured = true;
   }
   const int tiles = ((p.Nout + BN - 1) / BN) * ((p.M + BM - 1) / BM);
   const int grid = 8 * ((tiles + 7) / 8);
-  hipLaunchKernelGGL((gemm_kernel<TW, LORA, VEC>), dim3(grid), dim3(NT), kSmemBytes, s, p);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, TW, LORA, VEC>), dim3(grid), dim3(NT), smem_bytes, s, p);
   return hipGetLastError();
 }
 
 template <bool TW, bool LORA>
 hipError_t launch_rows(const GemmParams& p, hipStream_t s) {
-  // reductions in whole 64-element steps take the DMA / uniform-address path
-  return (p.Kred % BK == 0) ? launch_variant<TW, LORA, true>(p, s) : launch_variant<TW, LORA, false>(p, s);
+  // reductions in whole 64-element steps take the DMA / uniform-address
+  // path; from 1024 rows on the 512 x 128 tile (half the unpacking per MFMA)
+  const bool vec = p.Kred % BK == 0;
+  if (p.M >= 1024)
+    return vec ? launch_variant<512, 128, TW, LORA, true>(p, s) : launch_variant<512, 128, TW, LORA, false>(p, s);
+  return vec ? launch_variant<256, 256, TW, LORA, true>(p, s) : launch_variant<256, 256, TW, LORA, false>(p, s);
 }
 
 }  // namespace
