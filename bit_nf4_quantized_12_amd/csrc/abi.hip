@@ -35,7 +35,8 @@ inline int grad_splits(int64_t M, int64_t C, int64_t rp) {
 struct Layout {
   // byte offsets into the workspace; kNone when unused
   size_t partT = 0, T32 = 0, Ts = 0, Bpad = 0;                       // forward
-  size_t Bt = 0, At = 0, partU = 0, U32 = 0, PtH = 0, PtL = 0, gpart = 0;  // backward
+  size_t Bt = 0, At = 0, partU = 0, U32 = 0, PtH = 0, PtL = 0, TtH = 0, TtL = 0;  // backward
+  size_t gpartA = 0, gpartB = 0;
   size_t fwd_total = 0, bwd_total = 0;
   int tsplit = 1, usplit = 1, sA = 1, sB = 1;
 };
@@ -63,8 +64,10 @@ Layout plan(int64_t M, int64_t N, int64_t K, int64_t r) {
   const int64_t Mp = cdiv(M, 64) * 64;
   L.PtH = o;   o = al256(o + (size_t)rp * Mp * 2);
   L.PtL = o;   o = al256(o + (size_t)rp * Mp * 2);
-  L.gpart = o;
-  o = al256(o + std::max((size_t)L.sA * rp * K * 4, (size_t)L.sB * rp * N * 4));
+  L.TtH = o;   o = al256(o + (size_t)rp * Mp * 2);
+  L.TtL = o;   o = al256(o + (size_t)rp * Mp * 2);
+  L.gpartA = o; o = al256(o + (size_t)L.sA * rp * K * 4);
+  L.gpartB = o; o = al256(o + (size_t)L.sB * rp * N * 4);
   L.bwd_total = o;
   return L;
 }
@@ -278,12 +281,16 @@ int qlora_linear_bwd(const qlora_nf4_weight* W, const void* X, const void* A, co
     uint16_t* At = reinterpret_cast<uint16_t*>(base + L.At);
     float* partU = reinterpret_cast<float*>(base + L.partU);
     float* U32 = reinterpret_cast<float*>(base + L.U32);
-    // hi / lo bf16 planes [Mp, rp] of s U, later of s T (rows past M zero);
+    // hi / lo bf16 planes [Mp, rp] of s U and of s T (rows past M zero);
     // the hi plane of s U is also the row operand of the dX epilogue
     const int Mp = (int)(cdiv(M, 64) * 64);
     uint16_t* PtH = reinterpret_cast<uint16_t*>(base + L.PtH);
     uint16_t* PtL = reinterpret_cast<uint16_t*>(base + L.PtL);
-    float* gpart = reinterpret_cast<float*>(base + L.gpart);
+    uint16_t* TtH = reinterpret_cast<uint16_t*>(base + L.TtH);
+    uint16_t* TtL = reinterpret_cast<uint16_t*>(base + L.TtL);
+    float* gpartA = reinterpret_cast<float*>(base + L.gpartA);
+    float* gpartB = reinterpret_cast<float*>(base + L.gpartB);
+    const bool streamed_dB = N % 8 == 0;  // dB through the transpose-read kernel
 
     // T (float32 [M, r]): saved by the forward, or recomputed
     const float* T = T_saved;
@@ -295,14 +302,17 @@ int qlora_linear_bwd(const qlora_nf4_weight* W, const void* X, const void* A, co
       QLORA_TRY(launch_finalize(partT, L.tsplit, (int)M, (int)M, (int)r, rp, 1.0f, T32, Ts, nullptr, s));
       T = T32;
     }
-    // U = dY B: B^T [r, N] is the row operand of the projection
-    QLORA_TRY(launch_relayout(Bh, N, r, r, true, Bt, r, N, N, s));
+    // U = dY B: B^T [r, N] is the row operand of the projection; A^T [K, rp]
+    // is the column operand of the dX epilogue (one launch for both)
+    QLORA_TRY(launch_transpose2(Bh, Ah, (int)N, (int)K, (int)r, rp, Bt, dX ? At : nullptr, s));
     QLORA_TRY(launch_proj(dYh, Bt, (int)M, (int)N, (int)r, rp, L.usplit, partU, s));
-    QLORA_TRY(launch_finalize(partU, L.usplit, (int)M, Mp, (int)r, rp, scale, U32, PtH, PtL, s));
+    if (streamed_dB)
+      QLORA_TRY(launch_finalize2(partU, L.usplit, (int)M, Mp, (int)r, rp, scale, U32, PtH, PtL, T, TtH, TtL, s));
+    else
+      QLORA_TRY(launch_finalize(partU, L.usplit, (int)M, Mp, (int)r, rp, scale, U32, PtH, PtL, s));
 
     if (dX) {
-      // dX = dY W~ + (s U) A; A^T [K, rp] is the column operand of the epilogue
-      QLORA_TRY(launch_relayout(Ah, r, K, K, true, At, K, rp, rp, s));
+      // dX = dY W~ + (s U) A
       GemmParams p;
       p.act = dYh;
       p.codes = W->codes;
@@ -322,15 +332,15 @@ int qlora_linear_bwd(const qlora_nf4_weight* W, const void* X, const void* A, co
     }
     // dA = (s U)^T X  [r, K] (K % 64 == 0); dB = s dY^T T  [N, r], computed as
     // ((s T)^T dY)^T. The rank-r factor enters as its hi + lo bf16 planes.
-    QLORA_TRY(launch_grad_tr(PtH, PtL, Xh, (int)M, Mp, (int)K, rp, L.sA, false, gpart, s));
-    QLORA_TRY(launch_grad_reduce(gpart, L.sA, (int)r, rp, (int)K, 1.0f, false, false, static_cast<uint16_t*>(dA), s));
-    if (N % 8 == 0) {
-      QLORA_TRY(launch_split_rows(T, (int)M, Mp, (int)r, rp, scale, PtH, PtL, s));
-      QLORA_TRY(launch_grad_tr(PtH, PtL, dYh, (int)M, Mp, (int)N, rp, L.sB, true, gpart, s));
-      QLORA_TRY(launch_grad_reduce(gpart, L.sB, (int)r, rp, (int)N, 1.0f, true, true, static_cast<uint16_t*>(dB), s));
+    QLORA_TRY(launch_grad_tr(PtH, PtL, Xh, (int)M, Mp, (int)K, rp, L.sA, false, gpartA, s));
+    if (streamed_dB) {
+      QLORA_TRY(launch_grad_tr(TtH, TtL, dYh, (int)M, Mp, (int)N, rp, L.sB, true, gpartB, s));
+      QLORA_TRY(launch_grad_reduce2(gpartA, L.sA, (int)K, static_cast<uint16_t*>(dA), gpartB, L.sB, (int)N,
+                                    static_cast<uint16_t*>(dB), (int)r, rp, 1.0f, s));
     } else {
-      QLORA_TRY(launch_grad(T, dYh, (int)M, (int)N, (int)r, rp, L.sB, gpart, s));
-      QLORA_TRY(launch_grad_reduce(gpart, L.sB, (int)r, rp, (int)N, scale, true, false, static_cast<uint16_t*>(dB), s));
+      QLORA_TRY(launch_grad_reduce(gpartA, L.sA, (int)r, rp, (int)K, 1.0f, false, false, static_cast<uint16_t*>(dA), s));
+      QLORA_TRY(launch_grad(T, dYh, (int)M, (int)N, (int)r, rp, L.sB, gpartB, s));
+      QLORA_TRY(launch_grad_reduce(gpartB, L.sB, (int)r, rp, (int)N, scale, true, false, static_cast<uint16_t*>(dB), s));
     }
     return QLORA_OK;
   } catch (...) {

@@ -32,13 +32,18 @@ hipError_t launch_grad(const float* P, const uint16_t* Q, int M, int C, int r, i
                        float* part, hipStream_t s);
 hipError_t launch_grad_reduce(const float* part, int nsplit, int r, int rp, int C, float scale,
                               bool transpose, bool part_trans, uint16_t* out, hipStream_t s);
-hipError_t launch_split_rows(const float* P, int M, int Mp, int r, int rp, float scale, uint16_t* hi,
-                             uint16_t* lo, hipStream_t s);
 hipError_t launch_grad_tr(const uint16_t* Ph, const uint16_t* Pl, const uint16_t* Q, int M, int Mp, int C,
                           int rp, int nsplit, bool trans, float* part, hipStream_t s);
 hipError_t launch_relayout(const uint16_t* in, int64_t rows_in, int64_t cols_in, int64_t ldi,
                            bool transpose, uint16_t* out, int64_t rows_out, int64_t cols_out,
                            int64_t ldo, hipStream_t s);
+hipError_t launch_transpose2(const uint16_t* B, const uint16_t* A, int N, int K, int r, int rp, uint16_t* Bt,
+                             uint16_t* At, hipStream_t s);
+hipError_t launch_finalize2(const float* part, int nsplit, int M, int Mp, int r, int rp, float scale,
+                            float* P32, uint16_t* Ph, uint16_t* Pl, const float* T, uint16_t* Th,
+                            uint16_t* Tl, hipStream_t s);
+hipError_t launch_grad_reduce2(const float* partA, int nsA, int C1, uint16_t* dA, const float* partB, int nsB,
+                               int C2, uint16_t* dB, int r, int rp, float scale, hipStream_t s);
 hipError_t launch_gemv(const uint16_t* X, const uint8_t* codes, const uint8_t* c2, const float* c1,
                        int N, int K, int M, const float* tpart, int tsplit, int rp, const uint16_t* B,
                        int r, float scale, uint16_t* Y, float* T_out, hipStream_t s);

@@ -326,21 +326,6 @@ __global__ __launch_bounds__(256) void grad_kernel(const float* __restrict__ P,
 
 // P [M, r] float32 -> Pt_hi, Pt_lo [rp, Mp] bf16 with Pt_hi + Pt_lo ~ P^T
 // to ~16 bits (hi = bf16(p), lo = bf16(p - hi)); zero for j >= r or m >= M.
-// hi / lo bf16 planes [Mp, rp] of scale * P, P float32 [M, r]; zero outside.
-__global__ __launch_bounds__(256) void split_rows_kernel(const float* __restrict__ P, int M, int Mp,
-                                                          int r, int rp, float scale,
-                                                          uint16_t* __restrict__ hi,
-                                                          uint16_t* __restrict__ lo) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)Mp * rp) return;
-  const int64_t m = idx / rp;
-  const int j = (int)(idx % rp);
-  const float v = (m < M && j < r) ? scale * P[m * r + j] : 0.0f;
-  const __bf16 h = (__bf16)v;
-  hi[idx] = __builtin_bit_cast(uint16_t, h);
-  lo[idx] = __builtin_bit_cast(uint16_t, (__bf16)(v - (float)h));
-}
-
 // part[s][j][c] (TRANS: part[s][c][j]) = sum over the rows m of slice s of
 // P[m][j] Q[m][c], with P = hi + lo, two bf16 planes [Mp, rp] (rows past M
 // zero) and Q [M, C] bf16, C % 8 == 0. A workgroup (8 waves) owns 64 j
@@ -534,6 +519,80 @@ __global__ __launch_bounds__(256) void relayout_kernel(const uint16_t* __restric
   out[i * ldo + j] = (si < rows_in && sj < cols_in) ? in[si * ldi + sj] : (uint16_t)0;
 }
 
+// The backward's two small transposes in one launch: Bt [r, N] = B^T and
+// At [K, rp] = A^T with zero columns r .. rp-1 (when At is not null).
+__global__ __launch_bounds__(256) void transpose2_kernel(const uint16_t* __restrict__ B,
+                                                          const uint16_t* __restrict__ A, int N,
+                                                          int K, int r, int rp,
+                                                          uint16_t* __restrict__ Bt,
+                                                          uint16_t* __restrict__ At) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int nb = r * N;
+  if (idx < nb) {
+    const int j = idx / N, n = idx - j * N;
+    Bt[idx] = B[n * r + j];
+    return;
+  }
+  const int ia = idx - nb;
+  if (!At || ia >= K * rp) return;
+  const int k = ia / rp, j = ia - k * rp;
+  At[ia] = j < r ? A[j * K + k] : (uint16_t)0;
+}
+
+// finalize_kernel for the U partials, and in the same launch the hi / lo
+// planes of scale * T (T float32 [M, r]) into Th / Tl, both [Mp, rp].
+__global__ __launch_bounds__(256) void finalize2_kernel(const float* __restrict__ part, int nsplit,
+                                                         int M, int Mp, int r, int rp, float scale,
+                                                         float* __restrict__ P32,
+                                                         uint16_t* __restrict__ Ph,
+                                                         uint16_t* __restrict__ Pl,
+                                                         const float* __restrict__ T,
+                                                         uint16_t* __restrict__ Th,
+                                                         uint16_t* __restrict__ Tl) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)Mp * rp) return;
+  const int64_t m = idx / rp;
+  const int j = (int)(idx % rp);
+  const bool ok = m < M && j < r;
+  float v = 0.0f;
+  if (ok) {
+    for (int sp = 0; sp < nsplit; ++sp) v += part[(int64_t)sp * M * rp + idx];
+    if (P32) P32[m * r + j] = v;
+  }
+  const float sv = ok ? scale * v : 0.0f;
+  const __bf16 h = (__bf16)sv;
+  Ph[idx] = __builtin_bit_cast(uint16_t, h);
+  Pl[idx] = __builtin_bit_cast(uint16_t, (__bf16)(sv - (float)h));
+  const float tv = ok ? scale * T[m * r + j] : 0.0f;
+  const __bf16 th = (__bf16)tv;
+  Th[idx] = __builtin_bit_cast(uint16_t, th);
+  Tl[idx] = __builtin_bit_cast(uint16_t, (__bf16)(tv - (float)th));
+}
+
+// Both adapter-gradient reductions in one launch: dA [r, C1] from partials
+// [s][rp][C1] (first r * C1 threads) and dB [C2, r] from partials
+// [s][C2][rp], each bf16(scale * sum over the slices).
+__global__ __launch_bounds__(256) void grad_reduce2_kernel(const float* __restrict__ partA, int nsA,
+                                                            int C1, uint16_t* __restrict__ dA,
+                                                            const float* __restrict__ partB, int nsB,
+                                                            int C2, uint16_t* __restrict__ dB, int r,
+                                                            int rp, float scale) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t na = (int64_t)r * C1;
+  float v = 0.0f;
+  if (idx < na) {
+    const int64_t j = idx / C1, c = idx % C1;
+    for (int sp = 0; sp < nsA; ++sp) v += partA[((int64_t)sp * rp + j) * C1 + c];
+    dA[idx] = __builtin_bit_cast(uint16_t, (__bf16)(scale * v));
+    return;
+  }
+  const int64_t ib = idx - na;
+  if (ib >= (int64_t)C2 * r) return;
+  const int64_t c = ib / r, j = ib % r;
+  for (int sp = 0; sp < nsB; ++sp) v += partB[((int64_t)sp * C2 + c) * rp + j];
+  dB[ib] = __builtin_bit_cast(uint16_t, (__bf16)(scale * v));
+}
+
 }  // namespace
 
 hipError_t launch_proj(const uint16_t* L, const uint16_t* R, int M, int Kr, int r, int rp,
@@ -579,14 +638,6 @@ hipError_t launch_grad_reduce(const float* part, int nsplit, int r, int rp, int 
   return hipGetLastError();
 }
 
-hipError_t launch_split_rows(const float* P, int M, int Mp, int r, int rp, float scale, uint16_t* hi,
-                             uint16_t* lo, hipStream_t s) {
-  const int64_t total = (int64_t)Mp * rp;
-  hipLaunchKernelGGL(split_rows_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, P, M, Mp, r,
-                     rp, scale, hi, lo);
-  return hipGetLastError();
-}
-
 hipError_t launch_grad_tr(const uint16_t* Ph, const uint16_t* Pl, const uint16_t* Q, int M, int Mp, int C,
                           int rp, int nsplit, bool trans, float* part, hipStream_t s) {
   static bool configured = false;  // benign race: every thread sets the same value
@@ -615,6 +666,31 @@ hipError_t launch_relayout(const uint16_t* in, int64_t rows_in, int64_t cols_in,
   const int64_t total = rows_out * cols_out;
   hipLaunchKernelGGL(relayout_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, in,
                      rows_in, cols_in, ldi, transpose, out, rows_out, cols_out, ldo);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose2(const uint16_t* B, const uint16_t* A, int N, int K, int r, int rp, uint16_t* Bt,
+                             uint16_t* At, hipStream_t s) {
+  const int64_t total = (int64_t)r * N + (At ? (int64_t)K * rp : 0);
+  hipLaunchKernelGGL(transpose2_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, B, A, N, K, r,
+                     rp, Bt, At);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize2(const float* part, int nsplit, int M, int Mp, int r, int rp, float scale,
+                            float* P32, uint16_t* Ph, uint16_t* Pl, const float* T, uint16_t* Th,
+                            uint16_t* Tl, hipStream_t s) {
+  const int64_t total = (int64_t)Mp * rp;
+  hipLaunchKernelGGL(finalize2_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, nsplit, M,
+                     Mp, r, rp, scale, P32, Ph, Pl, T, Th, Tl);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_reduce2(const float* partA, int nsA, int C1, uint16_t* dA, const float* partB, int nsB,
+                               int C2, uint16_t* dB, int r, int rp, float scale, hipStream_t s) {
+  const int64_t total = (int64_t)r * C1 + (int64_t)C2 * r;
+  hipLaunchKernelGGL(grad_reduce2_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, partA, nsA,
+                     C1, dA, partB, nsB, C2, dB, r, rp, scale);
   return hipGetLastError();
 }
 
