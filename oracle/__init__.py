@@ -13,7 +13,8 @@ Parity pins: every public function here is pinned by tests under
 ``tests/test_oracle_*.py`` against facts fixed outside this module (library
 routines, closed forms, brute force, invariants). The one choice no page
 fixes -- the tail probability ``DELTA`` of the level construction -- is a
-reading and is flagged as such where it is defined.
+reading and is flagged as such where it is defined, as are the Int4 and FP4
+data types the pages compare NF4 with but do not define.
 """
 
 from .nf4_oracle import (  # noqa: F401
@@ -28,6 +29,12 @@ from .nf4_oracle import (  # noqa: F401
     bf16_round,
     quantize_nf4_dq,
     dequant,
+    int4_levels,
+    e2m1_decode,
+    fp4_levels,
+    codebook_levels,
+    quantize_blockwise,
+    dequant_blockwise,
     unpack_codes,
     storage_bits_per_param,
     linear_fwd,

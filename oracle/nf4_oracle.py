@@ -233,6 +233,92 @@ def quantize_nf4_dq(w, levels=None):
     return packed, c2, c1
 
 
+# ---------------------------------------------------------------------------
+# The 4-bit data types NF4 is compared with ("Introduction", contribution (1):
+# NF4 gives better empirical results than 4-bit Integers and 4-bit Floats).
+# The pages name these types but do not define them. READINGS: the plainest
+# common ones, normalised like NF4 into [-1, 1] by the block absmax, with the
+# exact zero at code 7 and the same nearest-value rule (a tie to the lower
+# code). Both have 15 distinct values; code 15 repeats +1 and is therefore
+# never chosen.
+# ---------------------------------------------------------------------------
+
+def int4_levels():
+    """Symmetric 4-bit integers k / 7, k = -7 .. 7 (code k + 7), as float32;
+    code 15 repeats +1."""
+    v = [k / 7.0 for k in range(-7, 8)] + [1.0]
+    return np.array(v, dtype=np.float64).astype(np.float32)
+
+
+def e2m1_decode(code):
+    """Value of a 4-bit float bit pattern: 1 sign bit, 2 exponent bits with
+    bias 1, 1 mantissa bit; exponent 0 is subnormal (0.5 * mantissa)."""
+    code = int(code)
+    sign, e, m = (code >> 3) & 1, (code >> 1) & 3, code & 1
+    mag = 0.5 * m if e == 0 else (1.0 + 0.5 * m) * 2.0 ** (e - 1)
+    return -mag if sign else mag
+
+
+def fp4_levels():
+    """The 15 distinct values of the 16 E2M1 bit patterns (+0 and -0 merge
+    into +0), ascending, divided by the largest magnitude 6, as float32;
+    code 15 repeats +1."""
+    vals = sorted({e2m1_decode(c) + 0.0 for c in range(16)})  # + 0.0 turns -0 into +0
+    assert len(vals) == 15
+    top = max(abs(v) for v in vals)
+    return (np.array(vals + [vals[-1]], dtype=np.float64) / top).astype(np.float32)
+
+
+def codebook_levels(name):
+    """Level table of a 4-bit data type by name: "nf4", "int4" or "fp4"."""
+    table = {"nf4": nf4_levels, "int4": int4_levels, "fp4": fp4_levels}
+    if name not in table:
+        raise ValueError("unknown 4-bit data type %r" % (name,))
+    return table[name]()
+
+
+def quantize_blockwise(w, levels=None):
+    """Blockwise 4-bit quantisation WITHOUT double quantisation: the baseline
+    the "Double Quantization" paragraph prices at 32/64 = 0.5 bit per weight.
+
+    Same codes as quantize_nf4_dq (exact per-block absmax, IEEE float32
+    quotient, nearest level); the constants are stored as they are: float32
+    absmax per block of 64. Returns ``(packed, absmax)``.
+    """
+    if levels is None:
+        levels = nf4_levels()
+    w = np.ascontiguousarray(w, dtype=np.float32).ravel()
+    if not np.all(np.isfinite(w)):
+        raise ValueError("weights must be finite")
+    n = w.size
+    if n == 0:
+        raise ValueError("empty input")
+    nb = -(-n // NF4_BLOCK)
+    padded = np.zeros(nb * NF4_BLOCK, dtype=np.float32)
+    padded[:n] = w
+    blocks = padded.reshape(nb, NF4_BLOCK)
+    codes = np.empty((nb, NF4_BLOCK), dtype=np.uint8)
+    absmax = np.empty(nb, dtype=np.float32)
+    step = 16384
+    for b0 in range(0, nb, step):
+        codes[b0:b0 + step], absmax[b0:b0 + step] = _codes_for_blocks(
+            blocks[b0:b0 + step], levels)
+    flat = codes.ravel()[:n]
+    if n % 2:
+        flat = np.concatenate([flat, np.zeros(1, dtype=np.uint8)])
+    packed = (flat[0::2] | (flat[1::2] << 4)).astype(np.uint8)
+    return packed, absmax
+
+
+def dequant_blockwise(packed, absmax, n, levels=None):
+    """W_hat_i = fp32(q[code_i] * absmax_b): one float32 product per weight."""
+    if levels is None:
+        levels = nf4_levels()
+    codes = unpack_codes(packed, n)
+    absmax = np.asarray(absmax, dtype=np.float32)
+    return (levels[codes] * absmax[np.arange(n) // NF4_BLOCK]).astype(np.float32)
+
+
 def unpack_codes(packed, n):
     """The n 4-bit codes stored in ``packed`` (inverse of the packing above)."""
     packed = np.asarray(packed, dtype=np.uint8)
@@ -262,10 +348,14 @@ def dequant(packed, c2, c1, n, levels=None):
     return (levels[codes] * chat_per_elem).astype(np.float32)
 
 
-def storage_bits_per_param(n):
-    """Stored bits per weight: 4-bit codes, one byte c2 per 64, fp32 c1 per 256 blocks."""
+def storage_bits_per_param(n, double_quant=True):
+    """Stored bits per weight: 4-bit codes plus, with double quantisation, one
+    byte c2 per 64 and an fp32 c1 per 256 blocks; without it, an fp32 absmax
+    per block of 64."""
     nb = -(-n // NF4_BLOCK)
     ng = -(-nb // DQ_BLOCK)
+    if not double_quant:
+        return (8.0 * (-(-n // 2)) + 32.0 * nb) / n
     return (8.0 * (-(-n // 2)) + 8.0 * nb + 32.0 * ng) / n
 
 
