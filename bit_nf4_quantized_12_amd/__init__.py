@@ -14,6 +14,12 @@ The function names are those of the C ABI (include/qlora.h):
 * ``qlora_linear_workspace_bytes(M, N, K, r)``
 * ``qlora_linear_fwd(W, X, A, B, scale, ...)``
 * ``qlora_linear_bwd(W, X, A, B, dY, T, scale, ...)``
+* ``qlora_levels(codebook)``, ``qlora_quantize_4bit(w, codebook, double_quant)``,
+  ``qlora_dequant_4bit(...)``: the Int4 / FP4 comparison types and the format
+  without double quantisation; a weight quantised that way carries its
+  ``codebook`` and ``double_quant`` and goes through ``qlora_4bit_matmul`` /
+  ``qlora_linear_fwd_4bit`` / ``qlora_linear_bwd_4bit`` (chosen by the wrappers
+  below from the weight).
 """
 
 import ctypes
@@ -28,6 +34,7 @@ LIB_PATH = os.path.join(_HERE, "libqlora.so")
 
 QLORA_F32 = 0
 QLORA_BF16 = 1
+CODEBOOKS = {"nf4": 0, "int4": 1, "fp4": 2}
 
 _lock = threading.Lock()
 _lib = None
@@ -44,6 +51,18 @@ class _Weight(ctypes.Structure):
         ("c1", ctypes.c_void_p),
         ("rows", ctypes.c_int64),
         ("cols", ctypes.c_int64),
+    ]
+
+
+class _Weight4bit(ctypes.Structure):
+    _fields_ = [
+        ("codes", ctypes.c_void_p),
+        ("consts", ctypes.c_void_p),
+        ("c1", ctypes.c_void_p),
+        ("rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64),
+        ("codebook", ctypes.c_int32),
+        ("double_quant", ctypes.c_int32),
     ]
 
 
@@ -67,6 +86,12 @@ def load_library(path=LIB_PATH):
             "qlora_linear_fwd": ([ctypes.POINTER(_Weight), vp, vp, vp, i64, i64, f32, vp, vp, vp, sz, vp], i32),
             "qlora_linear_bwd": ([ctypes.POINTER(_Weight), vp, vp, vp, vp, vp, i64, i64, f32, vp, vp, vp, vp, sz, vp], i32),
             "qlora_status_string": ([i32], ctypes.c_char_p),
+            "qlora_levels": ([i32, ctypes.POINTER(ctypes.c_float)], i32),
+            "qlora_quantize_4bit": ([vp, i64, i32, i32, vp, vp, vp, vp], i32),
+            "qlora_dequant_4bit": ([vp, vp, vp, i64, i32, i32, i32, vp, vp], i32),
+            "qlora_4bit_matmul": ([ctypes.POINTER(_Weight4bit), vp, i64, i32, vp, vp], i32),
+            "qlora_linear_fwd_4bit": ([ctypes.POINTER(_Weight4bit), vp, vp, vp, i64, i64, f32, vp, vp, vp, sz, vp], i32),
+            "qlora_linear_bwd_4bit": ([ctypes.POINTER(_Weight4bit), vp, vp, vp, vp, vp, i64, i64, f32, vp, vp, vp, vp, sz, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -99,8 +124,18 @@ def _need(t, dtype, name):
         raise ValueError(f"{name} must be contiguous")
 
 
-NF4Weight = namedtuple("NF4Weight", ["codes", "c2", "c1", "rows", "cols"])
-NF4Weight.__doc__ = "Stored NF4 + DQ weight [rows, cols]: device tensors codes (uint8), c2 (uint8), c1 (float32)."
+NF4Weight = namedtuple("NF4Weight", ["codes", "c2", "c1", "rows", "cols", "codebook", "double_quant"],
+                       defaults=("nf4", True))
+NF4Weight.__doc__ = (
+    "Stored 4-bit weight [rows, cols]: device tensors codes (uint8) and, with double quantisation, "
+    "c2 (uint8) and c1 (float32); without it, c2 holds the float32 block absmax and c1 is None. "
+    "codebook: 'nf4' (default), 'int4' or 'fp4'.")
+
+
+def _codebook_id(codebook):
+    if codebook not in CODEBOOKS:
+        raise ValueError(f"codebook must be one of {sorted(CODEBOOKS)}")
+    return CODEBOOKS[codebook]
 
 
 def storage_sizes(n):
@@ -136,12 +171,70 @@ def qlora_quantize_nf4_dq(w, out=None):
     return codes, c2, c1
 
 
-def quantize_weight(w):
-    """Quantise a 2-D bf16 weight [N, K] into an NF4Weight."""
+def qlora_levels(codebook="nf4"):
+    """The 16 levels (float32, ascending) of a 4-bit data type as a CPU tensor."""
+    out = (ctypes.c_float * 16)()
+    _check(load_library().qlora_levels(_codebook_id(codebook), out))
+    return torch.tensor(list(out), dtype=torch.float32)
+
+
+def qlora_quantize_4bit(w, codebook="nf4", double_quant=True, out=None):
+    """Quantise bf16 weights with a 4-bit data type -> (codes, consts, c1).
+
+    consts is c2 (uint8, E4M3) with double quantisation, else the float32 block
+    absmax; c1 is None without double quantisation.
+    """
+    _need(w, torch.bfloat16, "w")
+    cb = _codebook_id(codebook)
+    n = w.numel()
+    nc, nb, ng = storage_sizes(n)
+    if out is None:
+        dev = w.device
+        codes = torch.empty(nc, dtype=torch.uint8, device=dev)
+        consts = torch.empty(nb, dtype=torch.uint8 if double_quant else torch.float32, device=dev)
+        c1 = torch.empty(ng, dtype=torch.float32, device=dev) if double_quant else None
+    else:
+        codes, consts, c1 = out
+    _check(load_library().qlora_quantize_4bit(_ptr(w), n, cb, 1 if double_quant else 0, _ptr(codes),
+                                              _ptr(consts), _ptr(c1), _stream(w.device)))
+    return codes, consts, c1
+
+
+def qlora_dequant_4bit(codes, consts, c1, n, codebook="nf4", double_quant=True, dtype=torch.float32,
+                       out=None):
+    """Dequantise n weights of a stored 4-bit format to float32 (W^) or bfloat16 (W~)."""
+    _need(codes, torch.uint8, "codes")
+    _need(consts, torch.uint8 if double_quant else torch.float32, "consts")
+    if double_quant:
+        _need(c1, torch.float32, "c1")
+    code = {torch.float32: QLORA_F32, torch.bfloat16: QLORA_BF16}.get(dtype)
+    if code is None:
+        raise TypeError("dtype must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty(n, dtype=dtype, device=codes.device)
+    _check(load_library().qlora_dequant_4bit(_ptr(codes), _ptr(consts), _ptr(c1) if double_quant else None, n,
+                                             _codebook_id(codebook), 1 if double_quant else 0, code,
+                                             _ptr(out), _stream(codes.device)))
+    return out
+
+
+def quantize_weight(w, codebook="nf4", double_quant=True):
+    """Quantise a 2-D bf16 weight [N, K] (NF4 + double quantisation by default)."""
     if w.dim() != 2:
         raise ValueError("weight must be 2-D [out, in]")
-    codes, c2, c1 = qlora_quantize_nf4_dq(w)
-    return NF4Weight(codes, c2, c1, w.shape[0], w.shape[1])
+    if codebook == "nf4" and double_quant:
+        codes, c2, c1 = qlora_quantize_nf4_dq(w)
+    else:
+        codes, c2, c1 = qlora_quantize_4bit(w, codebook, double_quant)
+    return NF4Weight(codes, c2, c1, w.shape[0], w.shape[1], codebook, bool(double_quant))
+
+
+def dequant_weight(W, dtype=torch.bfloat16):
+    """The dequantised weight [rows, cols] of a stored weight."""
+    n = W.rows * W.cols
+    if W.codebook == "nf4" and W.double_quant:
+        return qlora_dequant(W.codes, W.c2, W.c1, n, dtype).view(W.rows, W.cols)
+    return qlora_dequant_4bit(W.codes, W.c2, W.c1, n, W.codebook, W.double_quant, dtype).view(W.rows, W.cols)
 
 
 def qlora_dequant(codes, c2, c1, n, dtype=torch.float32, out=None):
@@ -167,21 +260,38 @@ def qlora_nf4_matmul(W, act, transposed=False, out=None):
         raise ValueError("act has the wrong number of columns")
     if out is None:
         out = torch.empty((M, W.cols if transposed else W.rows), dtype=torch.bfloat16, device=act.device)
-    w = _weight_struct(W)
-    _check(load_library().qlora_nf4_matmul(ctypes.byref(w), _ptr(act), M, 1 if transposed else 0,
-                                           _ptr(out), _stream(act.device)))
+    w, sfx = _weight_struct(W)
+    fn = load_library().qlora_nf4_matmul if not sfx else load_library().qlora_4bit_matmul
+    _check(fn(ctypes.byref(w), _ptr(act), M, 1 if transposed else 0, _ptr(out), _stream(act.device)))
     return out
+
+
+qlora_4bit_matmul = qlora_nf4_matmul  # one wrapper serves every stored format
 
 
 def qlora_linear_workspace_bytes(M, N, K, r):
     return int(load_library().qlora_linear_workspace_bytes(M, N, K, r))
 
 
+def _is_nf4_dq(W):
+    return W.codebook == "nf4" and W.double_quant
+
+
 def _weight_struct(W):
+    """(struct, entry-point suffix): the NF4 + DQ struct, or the general 4-bit one."""
     _need(W.codes, torch.uint8, "W.codes")
-    _need(W.c2, torch.uint8, "W.c2")
-    _need(W.c1, torch.float32, "W.c1")
-    return _Weight(W.codes.data_ptr(), W.c2.data_ptr(), W.c1.data_ptr(), W.rows, W.cols)
+    if _is_nf4_dq(W):
+        _need(W.c2, torch.uint8, "W.c2")
+        _need(W.c1, torch.float32, "W.c1")
+        return _Weight(W.codes.data_ptr(), W.c2.data_ptr(), W.c1.data_ptr(), W.rows, W.cols), ""
+    if W.double_quant:
+        _need(W.c2, torch.uint8, "W.c2")
+        _need(W.c1, torch.float32, "W.c1")
+    else:
+        _need(W.c2, torch.float32, "W.c2 (block absmax)")
+    c1 = W.c1.data_ptr() if W.double_quant else None
+    return _Weight4bit(W.codes.data_ptr(), W.c2.data_ptr(), c1, W.rows, W.cols,
+                       _codebook_id(W.codebook), 1 if W.double_quant else 0), "_4bit"
 
 
 def _workspace(M, N, K, r, device, workspace):
@@ -208,10 +318,10 @@ def qlora_linear_fwd(W, X, A, B, scale, save_T=True, Y=None, T=None, workspace=N
     if not save_T:
         T = None
     ws = _workspace(M, W.rows, K, r, dev, workspace)
-    w = _weight_struct(W)
-    _check(load_library().qlora_linear_fwd(ctypes.byref(w), _ptr(X), _ptr(A), _ptr(B), M, r,
-                                           float(scale), _ptr(Y), _ptr(T), _ptr(ws), ws.numel(),
-                                           _stream(dev)))
+    w, sfx = _weight_struct(W)
+    fn = getattr(load_library(), "qlora_linear_fwd" + sfx)
+    _check(fn(ctypes.byref(w), _ptr(X), _ptr(A), _ptr(B), M, r, float(scale), _ptr(Y), _ptr(T), _ptr(ws),
+              ws.numel(), _stream(dev)))
     return Y, T
 
 
@@ -237,10 +347,10 @@ def qlora_linear_bwd(W, X, A, B, dY, T, scale, need_dX=True, dX=None, dA=None, d
     if dB is None:
         dB = torch.empty((N, r), dtype=torch.bfloat16, device=dev)
     ws = _workspace(M, N, K, r, dev, workspace)
-    w = _weight_struct(W)
-    _check(load_library().qlora_linear_bwd(ctypes.byref(w), _ptr(X), _ptr(A), _ptr(B), _ptr(dY),
-                                           _ptr(T), M, r, float(scale), _ptr(dX), _ptr(dA),
-                                           _ptr(dB), _ptr(ws), ws.numel(), _stream(dev)))
+    w, sfx = _weight_struct(W)
+    fn = getattr(load_library(), "qlora_linear_bwd" + sfx)
+    _check(fn(ctypes.byref(w), _ptr(X), _ptr(A), _ptr(B), _ptr(dY), _ptr(T), M, r, float(scale), _ptr(dX),
+              _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(), _stream(dev)))
     return dX, dA, dB
 
 
@@ -261,3 +371,8 @@ class LoRALinear4bitFunction(torch.autograd.Function):
         dX, dA, dB = qlora_linear_bwd(ctx.W, X, A, B, dY.contiguous(), T, ctx.scale,
                                       need_dX=ctx.needs_input_grad[0])
         return dX, dA, dB, None, None
+
+
+# the general-format entry points have the same wrappers (dispatch on the weight)
+qlora_linear_fwd_4bit = qlora_linear_fwd
+qlora_linear_bwd_4bit = qlora_linear_bwd

@@ -72,16 +72,62 @@ Layout plan(int64_t M, int64_t N, int64_t K, int64_t r) {
   return L;
 }
 
-int check_linear(const qlora_nf4_weight* W, const void* X, const void* A, const void* B,
-                 int64_t M, int64_t r, float scale, const void* ws, size_t ws_bytes) {
-  if (!W || !X || !A || !B) return QLORA_ERR_NULL;
+// A stored weight in any supported format: double-quantised constants
+// (c2, c1) or fp32 block absmax, and a level table.
+struct WView {
+  const uint8_t* codes = nullptr;
+  const uint8_t* c2 = nullptr;
+  const float* c1 = nullptr;
+  const float* absmax = nullptr;
+  int64_t N = 0, K = 0;
+  int cb = kNF4;
+};
+
+int view_nf4(const qlora_nf4_weight* W, WView& v) {
+  if (!W) return QLORA_ERR_NULL;
   if (!W->codes || !W->c2_fp8 || !W->c1) return QLORA_ERR_NULL;
-  const int64_t N = W->rows, K = W->cols;
+  if (!aligned(W->codes, 16) || !aligned(W->c2_fp8, 16) || !aligned(W->c1, 4)) return QLORA_ERR_ALIGN;
+  v.codes = W->codes;
+  v.c2 = W->c2_fp8;
+  v.c1 = W->c1;
+  v.absmax = nullptr;
+  v.N = W->rows;
+  v.K = W->cols;
+  v.cb = kNF4;
+  return QLORA_OK;
+}
+
+int check_format(int codebook, int double_quant) {
+  if (codebook < 0 || codebook >= kNumCodebooks) return QLORA_ERR_UNSUPPORTED;
+  if (double_quant != 0 && double_quant != 1) return QLORA_ERR_UNSUPPORTED;
+  return QLORA_OK;
+}
+
+int view_4bit(const qlora_4bit_weight* W, WView& v) {
+  if (!W) return QLORA_ERR_NULL;
+  const int f = check_format(W->codebook, W->double_quant);
+  if (f != QLORA_OK) return f;
+  if (!W->codes || !W->consts || (W->double_quant && !W->c1)) return QLORA_ERR_NULL;
+  if (!aligned(W->codes, 16) || !aligned(W->consts, 16) || (W->double_quant && !aligned(W->c1, 4)))
+    return QLORA_ERR_ALIGN;
+  v.codes = W->codes;
+  v.c2 = W->double_quant ? static_cast<const uint8_t*>(W->consts) : nullptr;
+  v.c1 = W->double_quant ? W->c1 : nullptr;
+  v.absmax = W->double_quant ? nullptr : static_cast<const float*>(W->consts);
+  v.N = W->rows;
+  v.K = W->cols;
+  v.cb = W->codebook;
+  return QLORA_OK;
+}
+
+int check_linear(const WView& W, const void* X, const void* A, const void* B,
+                 int64_t M, int64_t r, float scale, const void* ws, size_t ws_bytes) {
+  if (!X || !A || !B) return QLORA_ERR_NULL;
+  const int64_t N = W.N, K = W.K;
   if (M < 1 || N < 1 || K < 64 || (K % 64) != 0) return QLORA_ERR_SHAPE;
   if (r < 1 || r > 256) return QLORA_ERR_SHAPE;
   if (M * std::max(N, K) >= (int64_t(1) << 31) || N * K >= (int64_t(1) << 40)) return QLORA_ERR_SHAPE;
   if (!std::isfinite(scale)) return QLORA_ERR_UNSUPPORTED;
-  if (!aligned(W->codes, 16) || !aligned(W->c2_fp8, 16) || !aligned(W->c1, 4)) return QLORA_ERR_ALIGN;
   if (!aligned(X, 16) || !aligned(A, 16) || !aligned(B, 16)) return QLORA_ERR_ALIGN;
   if (!ws) return QLORA_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return QLORA_ERR_ALIGN;
@@ -94,83 +140,21 @@ int check_linear(const qlora_nf4_weight* W, const void* X, const void* A, const 
     if ((expr) != hipSuccess) return QLORA_ERR_DEVICE; \
   } while (0)
 
-}  // namespace
-
-extern "C" {
-
-int qlora_nf4_levels(float out[16]) {
-  if (!out) return QLORA_ERR_NULL;
-  try {
-    if (tables_status() != 0) return QLORA_ERR_UNSUPPORTED;
-    const Levels& lv = host_levels();
-    for (int i = 0; i < 16; ++i) out[i] = lv.q[i];
-    return QLORA_OK;
-  } catch (...) {
-    return QLORA_ERR_DEVICE;
-  }
-}
-
-const char* qlora_status_string(int status) {
-  switch (status) {
-    case QLORA_OK: return "ok";
-    case QLORA_ERR_NULL: return "null pointer argument";
-    case QLORA_ERR_SHAPE: return "size out of range or inconsistent";
-    case QLORA_ERR_ALIGN: return "pointer not aligned (16 bytes; 4 for c1/T; 256 for workspace)";
-    case QLORA_ERR_UNSUPPORTED: return "unsupported mode or value";
-    case QLORA_ERR_WORKSPACE: return "workspace missing or too small";
-    case QLORA_ERR_DEVICE: return "HIP call failed";
-    default: return "unknown status";
-  }
-}
-
-int qlora_quantize_nf4_dq(const void* w_bf16, int64_t n, uint8_t* codes, uint8_t* c2_fp8,
-                          float* c1, void* stream) {
-  if (!w_bf16 || !codes || !c2_fp8 || !c1) return QLORA_ERR_NULL;
-  if (n < 1) return QLORA_ERR_SHAPE;
-  if (!aligned(w_bf16, 16) || !aligned(codes, 16) || !aligned(c2_fp8, 16) || !aligned(c1, 4))
-    return QLORA_ERR_ALIGN;
-  try {
-    if (tables_status() != 0) return QLORA_ERR_UNSUPPORTED;
-    QLORA_TRY(launch_quantize(w_bf16, n, codes, c2_fp8, c1, (hipStream_t)stream));
-    return QLORA_OK;
-  } catch (...) {
-    return QLORA_ERR_DEVICE;
-  }
-}
-
-int qlora_dequant(const uint8_t* codes, const uint8_t* c2_fp8, const float* c1, int64_t n,
-                  int out_dtype, void* out, void* stream) {
-  if (!codes || !c2_fp8 || !c1 || !out) return QLORA_ERR_NULL;
-  if (n < 1) return QLORA_ERR_SHAPE;
-  if (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16) return QLORA_ERR_UNSUPPORTED;
-  if (!aligned(codes, 16) || !aligned(c2_fp8, 16) || !aligned(c1, 4) || !aligned(out, 16))
-    return QLORA_ERR_ALIGN;
-  try {
-    if (tables_status() != 0) return QLORA_ERR_UNSUPPORTED;
-    QLORA_TRY(launch_dequant(codes, c2_fp8, c1, n, out_dtype == QLORA_BF16, out, (hipStream_t)stream));
-    return QLORA_OK;
-  } catch (...) {
-    return QLORA_ERR_DEVICE;
-  }
-}
-
-int qlora_nf4_matmul(const qlora_nf4_weight* W, const void* act, int64_t M, int transposed,
-                     void* out, void* stream) {
-  if (!W || !act || !out || !W->codes || !W->c2_fp8 || !W->c1) return QLORA_ERR_NULL;
-  const int64_t N = W->rows, K = W->cols;
+int matmul_impl(const WView& W, const void* act, int64_t M, int transposed, void* out, void* stream) {
+  if (!act || !out) return QLORA_ERR_NULL;
+  const int64_t N = W.N, K = W.K;
   if (M < 1 || N < 1 || K < 64 || (K % 64) != 0) return QLORA_ERR_SHAPE;
   if (transposed != 0 && transposed != 1) return QLORA_ERR_UNSUPPORTED;
   if (M * std::max(N, K) >= (int64_t(1) << 31) || N * K >= (int64_t(1) << 40)) return QLORA_ERR_SHAPE;
-  if (!aligned(W->codes, 16) || !aligned(W->c2_fp8, 16) || !aligned(W->c1, 4) ||
-      !aligned(act, 16) || !aligned(out, 16))
-    return QLORA_ERR_ALIGN;
+  if (!aligned(act, 16) || !aligned(out, 16)) return QLORA_ERR_ALIGN;
   try {
     if (tables_status() != 0) return QLORA_ERR_UNSUPPORTED;
     GemmParams p;
     p.act = static_cast<const uint16_t*>(act);
-    p.codes = W->codes;
-    p.c2 = W->c2_fp8;
-    p.c1 = W->c1;
+    p.codes = W.codes;
+    p.c2 = W.c2;
+    p.c1 = W.c1;
+    p.absmax = W.absmax;
     p.wN = N;
     p.wK = K;
     p.lora_l = nullptr;
@@ -180,7 +164,7 @@ int qlora_nf4_matmul(const qlora_nf4_weight* W, const void* act, int64_t M, int 
     p.M = (int)M;
     p.Nout = (int)(transposed ? K : N);
     p.Kred = (int)(transposed ? N : K);
-    p.lv = host_levels();
+    p.lv = host_levels(W.cb);
     QLORA_TRY(launch_gemm(p, transposed == 1, (hipStream_t)stream));
     return QLORA_OK;
   } catch (...) {
@@ -188,21 +172,13 @@ int qlora_nf4_matmul(const qlora_nf4_weight* W, const void* act, int64_t M, int 
   }
 }
 
-size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
-  if (M < 1 || N < 1 || K < 64 || (K % 64) != 0 || r < 1 || r > 256) return 0;
-  if (M * std::max(N, K) >= (int64_t(1) << 31)) return 0;
-  const Layout L = plan(M, N, K, r);
-  return std::max(L.fwd_total, L.bwd_total);
-}
-
-int qlora_linear_fwd(const qlora_nf4_weight* W, const void* X, const void* A, const void* B,
-                     int64_t M, int64_t r, float scale, void* Y, float* T_save, void* ws,
-                     size_t ws_bytes, void* stream) {
+int fwd_impl(const WView& W, const void* X, const void* A, const void* B, int64_t M, int64_t r, float scale,
+             void* Y, float* T_save, void* ws, size_t ws_bytes, void* stream) {
   int st = check_linear(W, X, A, B, M, r, scale, ws, ws_bytes);
   if (st != QLORA_OK) return st;
   if (!Y) return QLORA_ERR_NULL;
   if (!aligned(Y, 16) || (T_save && !aligned(T_save, 4))) return QLORA_ERR_ALIGN;
-  const int64_t N = W->rows, K = W->cols;
+  const int64_t N = W.N, K = W.K;
   const Layout L = plan(M, N, K, r);
   if (ws_bytes < L.fwd_total) return QLORA_ERR_WORKSPACE;
   try {
@@ -222,8 +198,8 @@ int qlora_linear_fwd(const qlora_nf4_weight* W, const void* X, const void* A, co
     if (M <= kGemvMaxM) {
       // few tokens: one weight-streaming kernel, which also sums the T
       // partials, adds the LoRA term and writes T_save
-      QLORA_TRY(launch_gemv(Xh, W->codes, W->c2_fp8, W->c1, (int)N, (int)K, (int)M, partT, L.tsplit, rp,
-                            Bh, (int)r, scale, static_cast<uint16_t*>(Y), T_save, s));
+      QLORA_TRY(launch_gemv(Xh, W.codes, W.c2, W.c1, W.absmax, W.cb, (int)N, (int)K, (int)M, partT, L.tsplit,
+                            rp, Bh, (int)r, scale, static_cast<uint16_t*>(Y), T_save, s));
       return QLORA_OK;
     }
     // Ts = bf16(scale * T) [M, rp], T float32 [M, r]
@@ -236,9 +212,10 @@ int qlora_linear_fwd(const qlora_nf4_weight* W, const void* X, const void* A, co
     }
     GemmParams p;
     p.act = Xh;
-    p.codes = W->codes;
-    p.c2 = W->c2_fp8;
-    p.c1 = W->c1;
+    p.codes = W.codes;
+    p.c2 = W.c2;
+    p.c1 = W.c1;
+    p.absmax = W.absmax;
     p.wN = N;
     p.wK = K;
     p.lora_l = Ts;
@@ -248,7 +225,7 @@ int qlora_linear_fwd(const qlora_nf4_weight* W, const void* X, const void* A, co
     p.M = (int)M;
     p.Nout = (int)N;
     p.Kred = (int)K;
-    p.lv = host_levels();
+    p.lv = host_levels(W.cb);
     QLORA_TRY(launch_gemm(p, false, s));
     return QLORA_OK;
   } catch (...) {
@@ -256,16 +233,16 @@ int qlora_linear_fwd(const qlora_nf4_weight* W, const void* X, const void* A, co
   }
 }
 
-int qlora_linear_bwd(const qlora_nf4_weight* W, const void* X, const void* A, const void* B,
-                     const void* dY, const float* T_saved, int64_t M, int64_t r, float scale,
-                     void* dX, void* dA, void* dB, void* ws, size_t ws_bytes, void* stream) {
+int bwd_impl(const WView& W, const void* X, const void* A, const void* B, const void* dY, const float* T_saved,
+             int64_t M, int64_t r, float scale, void* dX, void* dA, void* dB, void* ws, size_t ws_bytes,
+             void* stream) {
   int st = check_linear(W, X, A, B, M, r, scale, ws, ws_bytes);
   if (st != QLORA_OK) return st;
   if (!dY || !dA || !dB) return QLORA_ERR_NULL;
   if (!aligned(dY, 16) || !aligned(dA, 16) || !aligned(dB, 16) || (dX && !aligned(dX, 16)) ||
       (T_saved && !aligned(T_saved, 4)))
     return QLORA_ERR_ALIGN;
-  const int64_t N = W->rows, K = W->cols;
+  const int64_t N = W.N, K = W.K;
   const Layout L = plan(M, N, K, r);
   if (ws_bytes < L.bwd_total) return QLORA_ERR_WORKSPACE;
   try {
@@ -315,9 +292,10 @@ int qlora_linear_bwd(const qlora_nf4_weight* W, const void* X, const void* A, co
       // dX = dY W~ + (s U) A
       GemmParams p;
       p.act = dYh;
-      p.codes = W->codes;
-      p.c2 = W->c2_fp8;
-      p.c1 = W->c1;
+      p.codes = W.codes;
+      p.c2 = W.c2;
+      p.c1 = W.c1;
+    p.absmax = W.absmax;
       p.wN = N;
       p.wK = K;
       p.lora_l = PtH;
@@ -327,7 +305,7 @@ int qlora_linear_bwd(const qlora_nf4_weight* W, const void* X, const void* A, co
       p.M = (int)M;
       p.Nout = (int)K;
       p.Kred = (int)N;
-      p.lv = host_levels();
+      p.lv = host_levels(W.cb);
       QLORA_TRY(launch_gemm(p, true, s));
     }
     // dA = (s U)^T X  [r, K] (K % 64 == 0); dB = s dY^T T  [N, r], computed as
@@ -346,6 +324,144 @@ int qlora_linear_bwd(const qlora_nf4_weight* W, const void* X, const void* A, co
   } catch (...) {
     return QLORA_ERR_DEVICE;
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+int qlora_levels(int codebook, float out[16]) {
+  if (!out) return QLORA_ERR_NULL;
+  if (codebook < 0 || codebook >= kNumCodebooks) return QLORA_ERR_UNSUPPORTED;
+  try {
+    if (tables_status() != 0) return QLORA_ERR_UNSUPPORTED;
+    const Levels& lv = host_levels(codebook);
+    for (int i = 0; i < 16; ++i) out[i] = lv.q[i];
+    return QLORA_OK;
+  } catch (...) {
+    return QLORA_ERR_DEVICE;
+  }
+}
+
+int qlora_nf4_levels(float out[16]) { return qlora_levels(kNF4, out); }
+
+const char* qlora_status_string(int status) {
+  switch (status) {
+    case QLORA_OK: return "ok";
+    case QLORA_ERR_NULL: return "null pointer argument";
+    case QLORA_ERR_SHAPE: return "size out of range or inconsistent";
+    case QLORA_ERR_ALIGN: return "pointer not aligned (16 bytes; 4 for c1/T; 256 for workspace)";
+    case QLORA_ERR_UNSUPPORTED: return "unsupported mode or value";
+    case QLORA_ERR_WORKSPACE: return "workspace missing or too small";
+    case QLORA_ERR_DEVICE: return "HIP call failed";
+    default: return "unknown status";
+  }
+}
+
+int qlora_quantize_4bit(const void* w_bf16, int64_t n, int codebook, int double_quant, uint8_t* codes,
+                        void* consts, float* c1, void* stream) {
+  const int f = check_format(codebook, double_quant);
+  if (f != QLORA_OK) return f;
+  if (!w_bf16 || !codes || !consts || (double_quant && !c1)) return QLORA_ERR_NULL;
+  if (n < 1) return QLORA_ERR_SHAPE;
+  if (!aligned(w_bf16, 16) || !aligned(codes, 16) || !aligned(consts, 16) || (double_quant && !aligned(c1, 4)))
+    return QLORA_ERR_ALIGN;
+  try {
+    if (tables_status() != 0) return QLORA_ERR_UNSUPPORTED;
+    uint8_t* c2 = double_quant ? static_cast<uint8_t*>(consts) : nullptr;
+    float* absmax = double_quant ? nullptr : static_cast<float*>(consts);
+    QLORA_TRY(launch_quantize(w_bf16, n, codebook, codes, c2, double_quant ? c1 : nullptr, absmax,
+                              (hipStream_t)stream));
+    return QLORA_OK;
+  } catch (...) {
+    return QLORA_ERR_DEVICE;
+  }
+}
+
+int qlora_quantize_nf4_dq(const void* w_bf16, int64_t n, uint8_t* codes, uint8_t* c2_fp8,
+                          float* c1, void* stream) {
+  if (!w_bf16 || !codes || !c2_fp8 || !c1) return QLORA_ERR_NULL;
+  return qlora_quantize_4bit(w_bf16, n, kNF4, 1, codes, c2_fp8, c1, stream);
+}
+
+int qlora_dequant_4bit(const uint8_t* codes, const void* consts, const float* c1, int64_t n, int codebook,
+                       int double_quant, int out_dtype, void* out, void* stream) {
+  const int f = check_format(codebook, double_quant);
+  if (f != QLORA_OK) return f;
+  if (!codes || !consts || (double_quant && !c1) || !out) return QLORA_ERR_NULL;
+  if (n < 1) return QLORA_ERR_SHAPE;
+  if (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16) return QLORA_ERR_UNSUPPORTED;
+  if (!aligned(codes, 16) || !aligned(consts, 16) || (double_quant && !aligned(c1, 4)) || !aligned(out, 16))
+    return QLORA_ERR_ALIGN;
+  try {
+    if (tables_status() != 0) return QLORA_ERR_UNSUPPORTED;
+    const uint8_t* c2 = double_quant ? static_cast<const uint8_t*>(consts) : nullptr;
+    const float* absmax = double_quant ? nullptr : static_cast<const float*>(consts);
+    QLORA_TRY(launch_dequant(codes, c2, double_quant ? c1 : nullptr, absmax, n, codebook, out_dtype == QLORA_BF16,
+                             out, (hipStream_t)stream));
+    return QLORA_OK;
+  } catch (...) {
+    return QLORA_ERR_DEVICE;
+  }
+}
+
+int qlora_dequant(const uint8_t* codes, const uint8_t* c2_fp8, const float* c1, int64_t n,
+                  int out_dtype, void* out, void* stream) {
+  if (!codes || !c2_fp8 || !c1 || !out) return QLORA_ERR_NULL;
+  return qlora_dequant_4bit(codes, c2_fp8, c1, n, kNF4, 1, out_dtype, out, stream);
+}
+
+int qlora_nf4_matmul(const qlora_nf4_weight* W, const void* act, int64_t M, int transposed,
+                     void* out, void* stream) {
+  WView v;
+  const int st = view_nf4(W, v);
+  return st != QLORA_OK ? st : matmul_impl(v, act, M, transposed, out, stream);
+}
+
+int qlora_4bit_matmul(const qlora_4bit_weight* W, const void* act, int64_t M, int transposed,
+                      void* out, void* stream) {
+  WView v;
+  const int st = view_4bit(W, v);
+  return st != QLORA_OK ? st : matmul_impl(v, act, M, transposed, out, stream);
+}
+
+size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
+  if (M < 1 || N < 1 || K < 64 || (K % 64) != 0 || r < 1 || r > 256) return 0;
+  if (M * std::max(N, K) >= (int64_t(1) << 31)) return 0;
+  const Layout L = plan(M, N, K, r);
+  return std::max(L.fwd_total, L.bwd_total);
+}
+
+int qlora_linear_fwd(const qlora_nf4_weight* W, const void* X, const void* A, const void* B,
+                     int64_t M, int64_t r, float scale, void* Y, float* T_save, void* ws,
+                     size_t ws_bytes, void* stream) {
+  WView v;
+  const int st = view_nf4(W, v);
+  return st != QLORA_OK ? st : fwd_impl(v, X, A, B, M, r, scale, Y, T_save, ws, ws_bytes, stream);
+}
+
+int qlora_linear_fwd_4bit(const qlora_4bit_weight* W, const void* X, const void* A, const void* B,
+                          int64_t M, int64_t r, float scale, void* Y, float* T_save, void* ws,
+                          size_t ws_bytes, void* stream) {
+  WView v;
+  const int st = view_4bit(W, v);
+  return st != QLORA_OK ? st : fwd_impl(v, X, A, B, M, r, scale, Y, T_save, ws, ws_bytes, stream);
+}
+
+int qlora_linear_bwd(const qlora_nf4_weight* W, const void* X, const void* A, const void* B,
+                     const void* dY, const float* T_saved, int64_t M, int64_t r, float scale,
+                     void* dX, void* dA, void* dB, void* ws, size_t ws_bytes, void* stream) {
+  WView v;
+  const int st = view_nf4(W, v);
+  return st != QLORA_OK ? st : bwd_impl(v, X, A, B, dY, T_saved, M, r, scale, dX, dA, dB, ws, ws_bytes, stream);
+}
+
+int qlora_linear_bwd_4bit(const qlora_4bit_weight* W, const void* X, const void* A, const void* B,
+                          const void* dY, const float* T_saved, int64_t M, int64_t r, float scale,
+                          void* dX, void* dA, void* dB, void* ws, size_t ws_bytes, void* stream) {
+  WView v;
+  const int st = view_4bit(W, v);
+  return st != QLORA_OK ? st : bwd_impl(v, X, A, B, dY, T_saved, M, r, scale, dX, dA, dB, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -21,19 +21,28 @@ struct Levels {
   float q[16];
 };
 
-// Nearest-level search table for the quantiser. [-1, 1] is cut into 32
-// equal cells; each cell holds at most one decision threshold (the fp32
-// value T with: code > j  <=>  x > T_j), so
-//   code(x) = base[cell(x)] + (x > thr[cell(x)]),  cell(x) = floor((x+1)*16).
+// 4-bit data types. NF4 is the pages' type; Int4 (k / 7, k = -7..7) and FP4
+// (the E2M1 values over 6) are the types the pages compare it with, in the
+// plainest common form (the pages do not define them). All three hold the
+// exact zero at code 7; Int4 and FP4 have 15 values and repeat +1 at code 15.
+enum Codebook { kNF4 = 0, kInt4 = 1, kFP4 = 2, kNumCodebooks = 3 };
+
+// Nearest-level search table for the quantiser. [-1, 1] is cut into
+// 2 * scale equal cells (at most 32); each cell holds at most one decision
+// threshold (the fp32 value T with: code > j  <=>  x > T_j), so
+//   code(x) = base[cell(x)] + (x > thr[cell(x)]),
+//   cell(x) = min(trunc(fma(x, scale, scale)), last).
 // Cells without a threshold carry thr = +2 (never exceeded).
 struct QuantTable {
   float thr[32];
   int32_t base[32];
+  float scale;
+  int32_t last;
 };
 
 // Host side (tables.hip). Built once, immutable afterwards.
-const Levels& host_levels();
-const QuantTable& host_quant_table();
+const Levels& host_levels(int codebook = kNF4);
+const QuantTable& host_quant_table(int codebook = kNF4);
 // Nonzero if the tables could not be built consistently.
 int tables_status();
 
@@ -69,6 +78,13 @@ __device__ __forceinline__ float block_scale(const uint8_t* __restrict__ c2,
   const float d = e4m3_value(c2[b]);
   const float g = c1[b >> 8];
   return __fmul_rn(d, g);
+}
+
+// Block constant without double quantisation (fp32 absmax stored as is)
+// when `absmax` is given, else the double-quantised one.
+__device__ __forceinline__ float block_const(const uint8_t* __restrict__ c2, const float* __restrict__ c1,
+                                             const float* __restrict__ absmax, int64_t b) {
+  return absmax ? absmax[b] : block_scale(c2, c1, b);
 }
 
 // LDS tiles of 64 bf16 per row (128 B) store the 16-byte chunk c of row R

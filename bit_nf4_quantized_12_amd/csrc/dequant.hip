@@ -1,8 +1,10 @@
-// Dequantisation of the stored NF4 + double-quantised format.
+// Dequantisation of the stored blockwise 4-bit formats (NF4, Int4 or FP4
+// levels; double-quantised constants or fp32 block absmax).
 //
 // "QLoRA: Efficient Finetuning of Quantized LLMs" (inquiringlines.com),
 // "Method": whenever a stored weight is used it is dequantised to BFloat16.
-// Per weight: W^ = fp32(q[code] * c^_b) with c^_b = fp32(e4m3(c2_b) * c1_g);
+// Per weight: W^ = fp32(q[code] * c^_b) with c^_b = fp32(e4m3(c2_b) * c1_g)
+// (c^_b = the stored fp32 absmax without double quantisation);
 // the bf16 output is W~ = bf16(W^), round to nearest even.
 //
 // Each lane turns one 4-byte word of codes (8 weights, inside one block)
@@ -35,7 +37,8 @@ __device__ __forceinline__ void emit8(void* __restrict__ out, int64_t e, uint32_
 template <bool BF16>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
                                                        const uint8_t* __restrict__ c2,
-                                                       const float* __restrict__ c1, int64_t n,
+                                                       const float* __restrict__ c1,
+                                                       const float* __restrict__ absmax, int64_t n,
                                                        void* __restrict__ out, Levels lv) {
   __shared__ float sq[16];
   if (threadIdx.x < 16) sq[threadIdx.x] = lv.q[threadIdx.x];
@@ -52,17 +55,17 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 #pragma unroll
     for (int u = 0; u < 4; ++u) wd[u] = cw[i + u * stride];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) cs[u] = block_scale(c2, c1, (i + u * stride) >> 3);
+    for (int u = 0; u < 4; ++u) cs[u] = block_const(c2, c1, absmax, (i + u * stride) >> 3);
 #pragma unroll
     for (int u = 0; u < 4; ++u) emit8<BF16>(out, (i + u * stride) * 8, wd[u], cs[u], sq);
   }
-  for (; i < nwords; i += stride) emit8<BF16>(out, i * 8, cw[i], block_scale(c2, c1, i >> 3), sq);
+  for (; i < nwords; i += stride) emit8<BF16>(out, i * 8, cw[i], block_const(c2, c1, absmax, i >> 3), sq);
 
   // short tail (n % 8 weights), one thread
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     for (int64_t e = nwords * 8; e < n; ++e) {
       const uint32_t code = (codes[e >> 1] >> (4 * (e & 1))) & 15u;
-      const float v = __fmul_rn(sq[code], block_scale(c2, c1, e >> 6));
+      const float v = __fmul_rn(sq[code], block_const(c2, c1, absmax, e >> 6));
       if (BF16) {
         const __bf16 h = (__bf16)v;
         reinterpret_cast<uint16_t*>(out)[e] = __builtin_bit_cast(uint16_t, h);
@@ -75,8 +78,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 
 }  // namespace
 
-hipError_t launch_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, int64_t n,
-                          bool bf16_out, void* out, hipStream_t s) {
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* absmax,
+                          int64_t n, int codebook, bool bf16_out, void* out, hipStream_t s) {
   const int64_t nwords = n >> 3;
   int64_t blocks = (nwords + 255) / 256;
   // a few resident waves per SIMD are enough for a streaming kernel;
@@ -86,10 +89,10 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* c2, const float* 
   if (blocks < 1) blocks = 1;
   if (bf16_out)
     hipLaunchKernelGGL(dequant_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, codes, c2, c1,
-                       n, out, host_levels());
+                       absmax, n, out, host_levels(codebook));
   else
     hipLaunchKernelGGL(dequant_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, codes, c2,
-                       c1, n, out, host_levels());
+                       c1, absmax, n, out, host_levels(codebook));
   return hipGetLastError();
 }
 

@@ -254,7 +254,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
       const int ke = min(kt, nk - 1);
       const int64_t e = (int64_t)ke * wstep + wbase;
       load_words<QW>(p.codes, e, h.c);
-      h.chat = block_scale(p.c2, p.c1, e >> 6);
+      h.chat = block_const(p.c2, p.c1, p.absmax, e >> 6);
     } else {
       // general reduction length: codes past the reduction end get c^ = 0
       // (their unpacked weights are exact zeros, which zero the reduction
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
       col = min(col, p.wK - 8 * QW);
       const int64_t e = n * p.wK + col;
       load_words<QW>(p.codes, e, h.c);
-      const float chat = block_scale(p.c2, p.c1, e >> 6);
+      const float chat = block_const(p.c2, p.c1, p.absmax, e >> 6);
       h.chat = ok ? chat : 0.0f;
     }
     return h;

@@ -10,6 +10,7 @@ struct GemmParams {
   const uint8_t* codes;    // NF4 codes of W [wN, wK]
   const uint8_t* c2;
   const float* c1;
+  const float* absmax;     // fp32 block constants (no double quantisation), or null
   int64_t wN, wK;
   const uint16_t* lora_l;  // [M, rp] bf16 (scale folded in), or null
   const uint16_t* lora_r;  // [Nout, rp] bf16, or null
@@ -19,10 +20,12 @@ struct GemmParams {
   Levels lv;
 };
 
-hipError_t launch_quantize(const void* w, int64_t n, uint8_t* codes, uint8_t* c2, float* c1,
-                           hipStream_t s);
-hipError_t launch_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, int64_t n,
-                          bool bf16_out, void* out, hipStream_t s);
+// Double-quantised constants (c2, c1) when absmax is null; otherwise the
+// fp32 block absmax, and c2 / c1 are unused.
+hipError_t launch_quantize(const void* w, int64_t n, int codebook, uint8_t* codes, uint8_t* c2, float* c1,
+                           float* absmax, hipStream_t s);
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* absmax,
+                          int64_t n, int codebook, bool bf16_out, void* out, hipStream_t s);
 hipError_t launch_gemm(const GemmParams& p, bool transposed_w, hipStream_t s);
 hipError_t launch_proj(const uint16_t* L, const uint16_t* R, int M, int Kr, int r, int rp,
                        int nsplit, float* part, hipStream_t s);
@@ -45,7 +48,7 @@ hipError_t launch_finalize2(const float* part, int nsplit, int M, int Mp, int r,
 hipError_t launch_grad_reduce2(const float* partA, int nsA, int C1, uint16_t* dA, const float* partB, int nsB,
                                int C2, uint16_t* dB, int r, int rp, float scale, hipStream_t s);
 hipError_t launch_gemv(const uint16_t* X, const uint8_t* codes, const uint8_t* c2, const float* c1,
-                       int N, int K, int M, const float* tpart, int tsplit, int rp, const uint16_t* B,
-                       int r, float scale, uint16_t* Y, float* T_out, hipStream_t s);
+                       const float* absmax, int codebook, int N, int K, int M, const float* tpart, int tsplit,
+                       int rp, const uint16_t* B, int r, float scale, uint16_t* Y, float* T_out, hipStream_t s);
 
 }  // namespace qlora

@@ -1,4 +1,5 @@
-// NF4 quantiser with double quantisation of the block constants.
+// Blockwise 4-bit quantiser (NF4, or the Int4 / FP4 comparison types) with
+// or without double quantisation of the block constants.
 //
 // "QLoRA: Efficient Finetuning of Quantized LLMs" (inquiringlines.com),
 // "Method": step (3) of "4-bit NormalFloat Quantization" (normalise each
@@ -9,7 +10,9 @@
 // of bf16. Loads are 16 B per lane and fully coalesced; the block absmax is
 // a max over the 8 lanes that hold a block (DPP, no LDS); the group max is a
 // wave reduction plus 4 LDS slots. HBM traffic is the algorithmic minimum:
-// 2 B read and 0.5 + 1/64 + 4/16384 B written per weight.
+// 2 B read and 0.5 + 1/64 + 4/16384 B written per weight (0.5 + 4/64 B
+// without double quantisation, when the fp32 block absmax is stored as is).
+// The data type only changes the search table passed in.
 #include "launch.hpp"
 
 namespace qlora {
@@ -43,9 +46,9 @@ __device__ __forceinline__ float div_block(float w, float c, float r, bool fast)
   return w / c;
 }
 
-__device__ __forceinline__ uint32_t nearest_code(float x, const float2* __restrict__ tab) {
-  int cell = (int)__builtin_fmaf(x, 16.0f, 16.0f);
-  cell = cell > 31 ? 31 : cell;
+__device__ __forceinline__ uint32_t nearest_code(float x, const float2* __restrict__ tab, float scale, int last) {
+  int cell = (int)__builtin_fmaf(x, scale, scale);
+  cell = cell > last ? last : cell;
   const float2 t = tab[cell];
   return (uint32_t)__float_as_int(t.y) + (x > t.x ? 1u : 0u);
 }
@@ -65,7 +68,8 @@ __device__ __forceinline__ uint32_t e4m3_code(float rho) {
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ w, int64_t n,
                                                         uint8_t* __restrict__ codes,
                                                         uint8_t* __restrict__ c2,
-                                                        float* __restrict__ c1, QuantTable qt) {
+                                                        float* __restrict__ c1,
+                                                        float* __restrict__ absmax_out, QuantTable qt) {
   __shared__ float2 s_tab[32];
   __shared__ float s_wmax[4];
   const int tid = threadIdx.x;
@@ -120,7 +124,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float x = div_block(f[i], m, r, fast);
-        word |= nearest_code(x, s_tab) << (4 * i);
+        word |= nearest_code(x, s_tab, qt.scale, qt.last) << (4 * i);
       }
     }
     if (full || e + 8 <= n) {
@@ -135,6 +139,17 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     }
   }
 
+  if (absmax_out) {
+    // no double quantisation: the exact block absmax is the stored constant
+    if ((lane & 7) == 0) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t b = (gbase >> 6) + wave * 64 + j * 8 + (lane >> 3);
+        if (b < nb) absmax_out[b] = bmax[j];
+      }
+    }
+    return;
+  }
   gmax = wave_max(gmax);
   if (lane == 0) s_wmax[wave] = gmax;
   __syncthreads();
@@ -155,11 +170,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
 
 }  // namespace
 
-hipError_t launch_quantize(const void* w, int64_t n, uint8_t* codes, uint8_t* c2, float* c1,
-                           hipStream_t s) {
+hipError_t launch_quantize(const void* w, int64_t n, int codebook, uint8_t* codes, uint8_t* c2, float* c1,
+                           float* absmax, hipStream_t s) {
   const int64_t groups = (n + kGroup - 1) / kGroup;
   hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)groups), dim3(256), 0, s,
-                     reinterpret_cast<const uint16_t*>(w), n, codes, c2, c1, host_quant_table());
+                     reinterpret_cast<const uint16_t*>(w), n, codes, c2, c1, absmax, host_quant_table(codebook));
   return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@
  *    the matmul operand is W~ = bf16(W^) (round to nearest even).
  *
  * Thread safety: every call may be made concurrently from several host
- * threads; the only global state is an immutable table built once.
+ * threads; the only global state is immutable tables built once.
  */
 #ifndef QLORA_H
 #define QLORA_H
@@ -148,6 +148,76 @@ int qlora_linear_bwd(const qlora_nf4_weight* W, const void* X, const void* A,
                      const void* B, const void* dY, const float* T_saved,
                      int64_t M, int64_t r, float scale, void* dX, void* dA,
                      void* dB, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Other 4-bit data types and the format without double quantisation.
+ *
+ * [P2] Introduction, contribution (1), compares NF4 with 4-bit Integers and
+ * 4-bit Floats; [P2] "Double Quantization" prices fp32 block constants at
+ * 32/64 = 0.5 bit per weight. The pages define neither comparison type; the
+ * library takes the plainest common forms (readings), normalised like NF4
+ * by the block absmax, with the exact zero at code 7 and the same nearest-
+ * value rule (a tie goes to the lower code):
+ *   QLORA_CB_NF4   the NF4 levels of qlora_nf4_levels
+ *   QLORA_CB_INT4  k / 7 for k = -7 .. 7 at code k + 7
+ *   QLORA_CB_FP4   the 15 distinct OCP E2M1 values (+-{0, .5, 1, 1.5, 2, 3,
+ *                  4, 6}) over 6, ascending
+ * Int4 and FP4 have 15 values; their code 15 repeats +1 and is never
+ * produced by the quantiser.
+ * Without double quantisation (double_quant = 0) the constants are the exact
+ * block absmax, float32[ceil(n/64)], and W^_i = fp32(q[code_i] * absmax_b).
+ * With it (double_quant = 1) they are c2 / c1 exactly as in the NF4 + DQ
+ * format above. The codes are the same either way.
+ * ------------------------------------------------------------------------- */
+typedef enum { QLORA_CB_NF4 = 0, QLORA_CB_INT4 = 1, QLORA_CB_FP4 = 2 } qlora_codebook;
+
+/* A quantised weight [rows=N, cols=K] in any supported format: views into
+ * caller-owned device memory for n = rows * cols.
+ *   consts: double_quant ? uint8 c2[ceil(n/64)] : float absmax[ceil(n/64)]
+ *   c1:     double_quant ? float[ceil(ceil(n/64)/256)] : unused (may be NULL) */
+typedef struct {
+  const uint8_t* codes;
+  const void* consts;
+  const float* c1;
+  int64_t rows;         /* N, out features */
+  int64_t cols;         /* K, in features  */
+  int32_t codebook;     /* qlora_codebook  */
+  int32_t double_quant; /* 1 or 0          */
+} qlora_4bit_weight;
+
+/* The 16 levels of a data type, ascending, as float32 (host memory).
+ * Synchronous, no GPU use. Errors: NULL, UNSUPPORTED (codebook). */
+int qlora_levels(int codebook, float out[16]);
+
+/* Quantise n bf16 weights with the given data type, with or without double
+ * quantisation of the block constants. Codes as for qlora_quantize_nf4_dq
+ * with the data type's levels. consts: device output, uint8[ceil(n/64)] (c2)
+ * or float[ceil(n/64)] (absmax); c1: device output float[ceil(ceil(n/64)/256)]
+ * when double_quant, else ignored. Alignment: w, codes, consts 16 bytes, c1
+ * 4 bytes. Errors: NULL, SHAPE (n < 1), ALIGN, UNSUPPORTED (codebook or
+ * double_quant out of range), DEVICE. */
+int qlora_quantize_4bit(const void* w_bf16, int64_t n, int codebook, int double_quant,
+                        uint8_t* codes, void* consts, float* c1, void* stream);
+
+/* Dequantise n weights of a stored 4-bit format to float32 (W^) or bf16
+ * (W~): [P2] "Method". Inputs as written by qlora_quantize_4bit with the
+ * same codebook and double_quant. Errors: NULL, SHAPE, ALIGN, UNSUPPORTED,
+ * DEVICE. */
+int qlora_dequant_4bit(const uint8_t* codes, const void* consts, const float* c1, int64_t n,
+                       int codebook, int double_quant, int out_dtype, void* out, void* stream);
+
+/* qlora_nf4_matmul, qlora_linear_fwd and qlora_linear_bwd for a weight in
+ * any supported format; arguments, limits, workspace and errors as there,
+ * plus UNSUPPORTED for a codebook or double_quant out of range. */
+int qlora_4bit_matmul(const qlora_4bit_weight* W, const void* act, int64_t M, int transposed,
+                      void* out, void* stream);
+int qlora_linear_fwd_4bit(const qlora_4bit_weight* W, const void* X, const void* A,
+                          const void* B, int64_t M, int64_t r, float scale, void* Y,
+                          float* T_save, void* ws, size_t ws_bytes, void* stream);
+int qlora_linear_bwd_4bit(const qlora_4bit_weight* W, const void* X, const void* A,
+                          const void* B, const void* dY, const float* T_saved,
+                          int64_t M, int64_t r, float scale, void* dX, void* dA,
+                          void* dB, void* ws, size_t ws_bytes, void* stream);
 
 /* Static text for a status code ("unknown status" for other values). */
 const char* qlora_status_string(int status);

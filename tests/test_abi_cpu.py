@@ -136,3 +136,63 @@ def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(TypeError):
         q.qlora_quantize_nf4_dq(torch.zeros(64, dtype=torch.bfloat16))
+
+
+# --- other 4-bit data types and the format without double quantisation ---
+
+@pytest.mark.parametrize("name", ["nf4", "int4", "fp4"])
+def test_codebook_levels_bit_exact_with_oracle(name):
+    got = q.qlora_levels(name).numpy()
+    np.testing.assert_array_equal(got.view(np.uint32), oracle.codebook_levels(name).view(np.uint32))
+
+
+def test_levels_validation(lib):
+    out = (ctypes.c_float * 16)()
+    assert lib.qlora_levels(0, None) == NULL
+    assert lib.qlora_levels(3, out) == UNSUPPORTED
+    assert lib.qlora_levels(-1, out) == UNSUPPORTED
+
+
+def test_quantize_4bit_validation(lib):
+    f = lib.qlora_quantize_4bit
+    assert f(FAKE, 64, 3, 1, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, 64, 0, 2, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(None, 64, 1, 0, FAKE, FAKE, None, None) == NULL
+    assert f(FAKE, 64, 1, 0, FAKE, None, None, None) == NULL
+    assert f(FAKE, 64, 1, 1, FAKE, FAKE, None, None) == NULL     # c1 needed with double quantisation
+    assert f(FAKE, 0, 2, 0, FAKE, FAKE, None, None) == SHAPE
+    assert f(FAKE, 64, 2, 0, FAKE, FAKE + 4, None, None) == ALIGN
+    assert f(FAKE, 64, 2, 1, FAKE, FAKE, FAKE + 2, None) == ALIGN
+
+
+def test_dequant_4bit_validation(lib):
+    f = lib.qlora_dequant_4bit
+    assert f(FAKE, FAKE, None, 64, 5, 0, 0, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, None, 64, 1, 1, 0, FAKE, None) == NULL
+    assert f(FAKE, None, None, 64, 1, 0, 0, FAKE, None) == NULL
+    assert f(FAKE, FAKE, None, 0, 1, 0, 0, FAKE, None) == SHAPE
+    assert f(FAKE, FAKE, None, 64, 1, 0, 9, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, FAKE + 8, None, 64, 1, 0, 0, FAKE, None) == ALIGN
+
+
+def _w4(rows, cols, codebook=1, dq=0, codes=FAKE, consts=FAKE, c1=None):
+    return q._Weight4bit(codes, consts, c1, rows, cols, codebook, dq)
+
+
+def test_linear_4bit_validation(lib):
+    fwd, bwd, mm = lib.qlora_linear_fwd_4bit, lib.qlora_linear_bwd_4bit, lib.qlora_4bit_matmul
+    ws = FAKE
+    args = (FAKE, FAKE, FAKE, 16, 8, ctypes.c_float(0.5), FAKE, None, ws, 1 << 30, None)
+    assert fwd(None, *args) == NULL
+    assert fwd(ctypes.byref(_w4(64, 64, codebook=7)), *args) == UNSUPPORTED
+    assert fwd(ctypes.byref(_w4(64, 64, dq=3)), *args) == UNSUPPORTED
+    assert fwd(ctypes.byref(_w4(64, 64, dq=1)), *args) == NULL          # c1 missing
+    assert fwd(ctypes.byref(_w4(64, 64, consts=None)), *args) == NULL
+    assert fwd(ctypes.byref(_w4(64, 64, consts=FAKE + 4)), *args) == ALIGN
+    assert fwd(ctypes.byref(_w4(64, 65)), *args) == SHAPE
+    bargs = (FAKE, FAKE, FAKE, FAKE, None, 16, 8, ctypes.c_float(0.5), FAKE, FAKE, FAKE, ws, 1 << 30, None)
+    assert bwd(ctypes.byref(_w4(64, 64, codebook=-1)), *bargs) == UNSUPPORTED
+    assert bwd(ctypes.byref(_w4(64, 64, codes=None)), *bargs) == NULL
+    assert mm(ctypes.byref(_w4(64, 64, codebook=3)), FAKE, 16, 0, FAKE, None) == UNSUPPORTED
+    assert mm(ctypes.byref(_w4(64, 64)), FAKE, 16, 2, FAKE, None) == UNSUPPORTED
+    assert mm(ctypes.byref(_w4(64, 64)), FAKE, 0, 0, FAKE, None) == SHAPE
