@@ -163,7 +163,7 @@ def main():
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                     "traffic": measured_traffic(),
-                    "kernel": "gemm_kernel<512, 128, false, false, true> (qlora_nf4_matmul, X W~^T)",
+                    "kernel": "gemm_kernel<512, 128, false, false, true, false> (qlora_nf4_matmul, X W~^T)",
                     "avg_launch_us": round(avg_s * 1e6, 2), "launches": launches,
                     "flops_per_launch": flops_per_launch}
         log(f"roofline kernel: avg {avg_s * 1e6:.1f} us/launch, {achieved:.1f} TFLOP/s")

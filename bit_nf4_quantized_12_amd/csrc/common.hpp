@@ -80,11 +80,14 @@ __device__ __forceinline__ float block_scale(const uint8_t* __restrict__ c2,
   return __fmul_rn(d, g);
 }
 
-// Block constant without double quantisation (fp32 absmax stored as is)
-// when `absmax` is given, else the double-quantised one.
+// Block constant: the fp32 absmax stored as is (ABS: no double
+// quantisation), else the double-quantised one. A template parameter rather
+// than a run-time test, so that hot loops stay one basic block.
+template <bool ABS>
 __device__ __forceinline__ float block_const(const uint8_t* __restrict__ c2, const float* __restrict__ c1,
                                              const float* __restrict__ absmax, int64_t b) {
-  return absmax ? absmax[b] : block_scale(c2, c1, b);
+  if (ABS) return absmax[b];
+  return block_scale(c2, c1, b);
 }
 
 // LDS tiles of 64 bf16 per row (128 B) store the 16-byte chunk c of row R

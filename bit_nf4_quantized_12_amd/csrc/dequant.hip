@@ -34,7 +34,7 @@ __device__ __forceinline__ void emit8(void* __restrict__ out, int64_t e, uint32_
   }
 }
 
-template <bool BF16>
+template <bool BF16, bool ABS>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
                                                        const uint8_t* __restrict__ c2,
                                                        const float* __restrict__ c1,
@@ -55,17 +55,17 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 #pragma unroll
     for (int u = 0; u < 4; ++u) wd[u] = cw[i + u * stride];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) cs[u] = block_const(c2, c1, absmax, (i + u * stride) >> 3);
+    for (int u = 0; u < 4; ++u) cs[u] = block_const<ABS>(c2, c1, absmax, (i + u * stride) >> 3);
 #pragma unroll
     for (int u = 0; u < 4; ++u) emit8<BF16>(out, (i + u * stride) * 8, wd[u], cs[u], sq);
   }
-  for (; i < nwords; i += stride) emit8<BF16>(out, i * 8, cw[i], block_const(c2, c1, absmax, i >> 3), sq);
+  for (; i < nwords; i += stride) emit8<BF16>(out, i * 8, cw[i], block_const<ABS>(c2, c1, absmax, i >> 3), sq);
 
   // short tail (n % 8 weights), one thread
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     for (int64_t e = nwords * 8; e < n; ++e) {
       const uint32_t code = (codes[e >> 1] >> (4 * (e & 1))) & 15u;
-      const float v = __fmul_rn(sq[code], block_const(c2, c1, absmax, e >> 6));
+      const float v = __fmul_rn(sq[code], block_const<ABS>(c2, c1, absmax, e >> 6));
       if (BF16) {
         const __bf16 h = (__bf16)v;
         reinterpret_cast<uint16_t*>(out)[e] = __builtin_bit_cast(uint16_t, h);
@@ -87,12 +87,16 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* c2, const float* 
   const int64_t cap = 256 * 16;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
-  if (bf16_out)
-    hipLaunchKernelGGL(dequant_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, codes, c2, c1,
-                       absmax, n, out, host_levels(codebook));
+  const Levels& lv = host_levels(codebook);
+  const dim3 g((unsigned)blocks), t(256);
+  if (bf16_out && absmax)
+    hipLaunchKernelGGL((dequant_kernel<true, true>), g, t, 0, s, codes, c2, c1, absmax, n, out, lv);
+  else if (bf16_out)
+    hipLaunchKernelGGL((dequant_kernel<true, false>), g, t, 0, s, codes, c2, c1, absmax, n, out, lv);
+  else if (absmax)
+    hipLaunchKernelGGL((dequant_kernel<false, true>), g, t, 0, s, codes, c2, c1, absmax, n, out, lv);
   else
-    hipLaunchKernelGGL(dequant_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, codes, c2,
-                       c1, absmax, n, out, host_levels(codebook));
+    hipLaunchKernelGGL((dequant_kernel<false, false>), g, t, 0, s, codes, c2, c1, absmax, n, out, lv);
   return hipGetLastError();
 }
 

@@ -179,7 +179,7 @@ __device__ __forceinline__ void load_words(const uint8_t* __restrict__ codes, in
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gbl_void_t;
 
-template <int BM, int BN, bool TW, bool LORA, bool VEC>
+template <int BM, int BN, bool TW, bool LORA, bool VEC, bool ABS>
 __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
   constexpr int WN = BN / 64;        // waves along the output columns
   constexpr int QW = BN / 64;        // code words unpacked per thread per step
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
       const int ke = min(kt, nk - 1);
       const int64_t e = (int64_t)ke * wstep + wbase;
       load_words<QW>(p.codes, e, h.c);
-      h.chat = block_const(p.c2, p.c1, p.absmax, e >> 6);
+      h.chat = block_const<ABS>(p.c2, p.c1, p.absmax, e >> 6);
     } else {
       // general reduction length: codes past the reduction end get c^ = 0
       // (their unpacked weights are exact zeros, which zero the reduction
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
       col = min(col, p.wK - 8 * QW);
       const int64_t e = n * p.wK + col;
       load_words<QW>(p.codes, e, h.c);
-      const float chat = block_const(p.c2, p.c1, p.absmax, e >> 6);
+      const float chat = block_const<ABS>(p.c2, p.c1, p.absmax, e >> 6);
       h.chat = ok ? chat : 0.0f;
     }
     return h;
@@ -379,38 +379,45 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
     }
 }
 
-template <int BM, int BN, bool TW, bool LORA, bool VEC>
+template <int BM, int BN, bool TW, bool LORA, bool VEC, bool ABS>
 hipError_t launch_variant(const GemmParams& p, hipStream_t s) {
   constexpr size_t smem_bytes = 2 * (BM + BN) * 64 * sizeof(uint16_t);
   static bool configured = false;  // benign race: every thread sets the same value
   if (!configured) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<BM, BN, TW, LORA, VEC>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<BM, BN, TW, LORA, VEC, ABS>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_bytes);
     if (e != hipSuccess) return e;
     configured = true;
   }
   const int tiles = ((p.Nout + BN - 1) / BN) * ((p.M + BM - 1) / BM);
   const int grid = 8 * ((tiles + 7) / 8);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, TW, LORA, VEC>), dim3(grid), dim3(NT), smem_bytes, s, p);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, TW, LORA, VEC, ABS>), dim3(grid), dim3(NT), smem_bytes, s, p);
   return hipGetLastError();
 }
 
-template <bool TW, bool LORA>
+template <bool TW, bool LORA, bool ABS>
 hipError_t launch_rows(const GemmParams& p, hipStream_t s) {
   // reductions in whole 64-element steps take the DMA / uniform-address
   // path; from 1024 rows on the 512 x 128 tile (half the unpacking per MFMA)
   const bool vec = p.Kred % BK == 0;
   if (p.M >= 1024)
-    return vec ? launch_variant<512, 128, TW, LORA, true>(p, s) : launch_variant<512, 128, TW, LORA, false>(p, s);
-  return vec ? launch_variant<256, 256, TW, LORA, true>(p, s) : launch_variant<256, 256, TW, LORA, false>(p, s);
+    return vec ? launch_variant<512, 128, TW, LORA, true, ABS>(p, s)
+               : launch_variant<512, 128, TW, LORA, false, ABS>(p, s);
+  return vec ? launch_variant<256, 256, TW, LORA, true, ABS>(p, s)
+             : launch_variant<256, 256, TW, LORA, false, ABS>(p, s);
+}
+
+template <bool TW, bool LORA>
+hipError_t launch_fmt(const GemmParams& p, hipStream_t s) {
+  return p.absmax ? launch_rows<TW, LORA, true>(p, s) : launch_rows<TW, LORA, false>(p, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const GemmParams& p, bool transposed_w, hipStream_t s) {
   const bool lora = p.lora_l != nullptr;
-  if (transposed_w) return lora ? launch_rows<true, true>(p, s) : launch_rows<true, false>(p, s);
-  return lora ? launch_rows<false, true>(p, s) : launch_rows<false, false>(p, s);
+  if (transposed_w) return lora ? launch_fmt<true, true>(p, s) : launch_fmt<true, false>(p, s);
+  return lora ? launch_fmt<false, true>(p, s) : launch_fmt<false, false>(p, s);
 }
 
 }  // namespace qlora

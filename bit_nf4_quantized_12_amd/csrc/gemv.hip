@@ -58,6 +58,7 @@ __device__ __forceinline__ uint4 gv_lookup8(uint32_t d, const uint32_t L[4], con
 
 constexpr int GV_WAVES = 16;
 
+template <bool ABS>
 __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ c2,
     const float* __restrict__ c1, const float* __restrict__ absmax, int N, int K, int M,
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
     kcc = kok ? kc : K - 32;
     const int64_t e = rowe + kcc;
     cw = *reinterpret_cast<const uint4*>(codes + (e >> 1));
-    const float s2 = block_const(c2, c1, absmax, e >> 6);
+    const float s2 = block_const<ABS>(c2, c1, absmax, e >> 6);
     chat = kok ? s2 : 0.0f;
   };
   auto chunk_mma = [&](const uint4& cw, float chat, int kcc, f32x4& acc) {
@@ -175,8 +176,12 @@ __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
 hipError_t launch_gemv(const uint16_t* X, const uint8_t* codes, const uint8_t* c2, const float* c1,
                        const float* absmax, int codebook, int N, int K, int M, const float* tpart, int tsplit,
                        int rp, const uint16_t* B, int r, float scale, uint16_t* Y, float* T_out, hipStream_t s) {
-  hipLaunchKernelGGL(gemv_kernel, dim3((N + 15) / 16), dim3(64 * GV_WAVES), 0, s, X, codes, c2, c1, absmax, N, K,
-                     M, tpart, tsplit, rp, B, r, scale, Y, T_out, host_levels(codebook));
+  if (absmax)
+    hipLaunchKernelGGL(gemv_kernel<true>, dim3((N + 15) / 16), dim3(64 * GV_WAVES), 0, s, X, codes, c2, c1, absmax,
+                       N, K, M, tpart, tsplit, rp, B, r, scale, Y, T_out, host_levels(codebook));
+  else
+    hipLaunchKernelGGL(gemv_kernel<false>, dim3((N + 15) / 16), dim3(64 * GV_WAVES), 0, s, X, codes, c2, c1, absmax,
+                       N, K, M, tpart, tsplit, rp, B, r, scale, Y, T_out, host_levels(codebook));
   return hipGetLastError();
 }
 

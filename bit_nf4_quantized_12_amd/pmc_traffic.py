@@ -24,7 +24,7 @@ import re
 import sys
 
 COPY_BYTES = 1 << 30
-ROOFLINE_KERNEL = "gemm_kernel<512, 128, false, false, true>"
+ROOFLINE_KERNEL = "gemm_kernel<512, 128, false, false, true, false>"
 GEMM_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "gemm.hip")
 
 
