@@ -22,6 +22,11 @@ Legs timed in the same run (HBM-bound rows of the path):
             its HBM traffic per launch comes from the FETCH_SIZE / WRITE_SIZE
             counter runs recorded in profiles/ (null when the GEMM source
             has changed since)
+  formats   the Int4 / FP4 comparison types and the format without double
+            quantisation beside NF4 + DQ: quantise and bf16-dequantise GB/s of
+            one 22016x8192 weight (each format's own bytes per weight), the
+            relative dequantisation error on N(0, 0.02) weights, bits per
+            weight, and the forward GEMM at 8192x4096x4096
   copycal   one elementwise pass reading and writing exactly 1 GiB each, the
             calibration point of those counters
             (see bit_nf4_quantized_12_amd/pmc_traffic.py)
@@ -53,7 +58,7 @@ def parse():
     ap.add_argument("--config", choices=["7b", "65b"], default="7b",
                     help="layer shapes of the step: LLaMA-7B (default) or 65B-class")
     ap.add_argument("--stack-layers", type=int, default=80, help="65B-class layers in the quantize leg")
-    ap.add_argument("--legs", default="roofline,quantize,gemv,gemm512",
+    ap.add_argument("--legs", default="roofline,quantize,gemv,gemm512,formats",
                     help="comma list of extra legs, or 'none'")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -280,6 +285,43 @@ def main():
                                           "GB/s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
         log(f"dequant bf16: {per * 1e3:.2f} ms, {gbs:.0f} GB/s")
         del stack, buf
+        torch.cuda.empty_cache()
+
+    # ---- the other 4-bit data types and the format without double quantisation ---------------
+    if "formats" in want:
+        Nf, Kf = 22016, 8192
+        w = synth.device_normal_bf16(Nf * Kf, 0.02, 2_000_001, dev).view(Nf, Kf)
+        wf = w.float()
+        ms2 = float((wf * wf).mean())
+        Xg = synth.device_normal_bf16(8192 * 4096, 1.0, 2_000_002, dev).view(8192, 4096)
+        wg = synth.device_normal_bf16(4096 * 4096, 0.02, 2_000_003, dev).view(4096, 4096)
+        og = torch.empty(8192, 4096, dtype=torch.bfloat16, device=dev)
+        fmt = {}
+        for cb in ("nf4", "int4", "fp4"):
+            for dq in (True, False):
+                key = f"{cb}_{'dq' if dq else 'fp32_absmax'}"
+                byts_w = 2.0 + 0.5 + ((1.0 / 64 + 4.0 / 16384) if dq else 4.0 / 64)
+                nw = Nf * Kf
+                W = q.quantize_weight(w, codebook=cb, double_quant=dq)
+                tq = timed(lambda: q.quantize_weight(w, codebook=cb, double_quant=dq), 3) / 3
+                d16 = torch.empty(Nf, Kf, dtype=torch.bfloat16, device=dev)
+                td = timed(lambda: q.qlora_dequant_4bit(W.codes, W.c2, W.c1, nw, cb, dq, torch.bfloat16,
+                                                        out=d16.view(-1)), 3) / 3
+                d32 = q.dequant_weight(W, torch.float32)
+                rel_mse = float(((d32 - wf) ** 2).mean()) / ms2
+                del d32, d16
+                Wg = q.quantize_weight(wg, codebook=cb, double_quant=dq)
+                q.qlora_nf4_matmul(Wg, Xg, False, out=og)
+                tg = timed(lambda: q.qlora_nf4_matmul(Wg, Xg, False, out=og), 5) / 5
+                fmt[key] = {"quantize_GB/s": round(nw * byts_w / tq / 1e9, 1),
+                            "dequant_bf16_GB/s": round(nw * byts_w / td / 1e9, 1),
+                            "rel_mse_vs_bf16_weights": round(rel_mse, 6),
+                            "bits_per_weight": round(4.0 + (8.0 / 64 + 32.0 / 16384 if dq else 32.0 / 64), 4),
+                            "gemm_8192x4096x4096_tflops": round(2.0 * 8192 * 4096 * 4096 / tg / 1e12, 1)}
+                log(f"format {key}: {fmt[key]}")
+                del W, Wg
+        legs["formats_22016x8192"] = fmt
+        del w, wf, Xg, wg, og
         torch.cuda.empty_cache()
 
     # ---- CPU oracle on a bounded sample of the step ---------------------------------------
