@@ -14,7 +14,8 @@ Parity pins: every public function here is pinned by tests under
 routines, closed forms, brute force, invariants). The one choice no page
 fixes -- the tail probability ``DELTA`` of the level construction -- is a
 reading and is flagged as such where it is defined, as are the Int4 and FP4
-data types the pages compare NF4 with but do not define.
+data types the pages compare NF4 with but do not define, and the optimizer
+update rule (the pages describe paged optimizer state, not the update).
 """
 
 from .nf4_oracle import (  # noqa: F401
@@ -40,3 +41,4 @@ from .nf4_oracle import (  # noqa: F401
     linear_fwd,
     linear_bwd,
 )
+from .adamw import adamw_step  # noqa: F401
