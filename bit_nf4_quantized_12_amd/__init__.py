@@ -14,6 +14,8 @@ The function names are those of the C ABI (include/qlora.h):
 * ``qlora_linear_workspace_bytes(M, N, K, r)``
 * ``qlora_linear_fwd(W, X, A, B, scale, ...)``
 * ``qlora_linear_bwd(W, X, A, B, dY, T, scale, ...)``
+* ``qlora_adamw_step(p32, grad, m, v, step, ...)``: the adapters' optimizer
+  step; the state may sit in HBM or in pinned host memory (paged out)
 * ``qlora_levels(codebook)``, ``qlora_quantize_4bit(w, codebook, double_quant)``,
   ``qlora_dequant_4bit(...)``: the Int4 / FP4 comparison types and the format
   without double quantisation; a weight quantised that way carries its
@@ -66,6 +68,17 @@ class _Weight4bit(ctypes.Structure):
     ]
 
 
+class _AdamWParams(ctypes.Structure):
+    _fields_ = [
+        ("lr", ctypes.c_float),
+        ("beta1", ctypes.c_float),
+        ("beta2", ctypes.c_float),
+        ("eps", ctypes.c_float),
+        ("weight_decay", ctypes.c_float),
+        ("step", ctypes.c_int64),
+    ]
+
+
 def load_library(path=LIB_PATH):
     """Load libqlora.so (once). Raises ImportError if it is missing or broken."""
     global _lib
@@ -87,6 +100,7 @@ def load_library(path=LIB_PATH):
             "qlora_linear_bwd": ([ctypes.POINTER(_Weight), vp, vp, vp, vp, vp, i64, i64, f32, vp, vp, vp, vp, sz, vp], i32),
             "qlora_status_string": ([i32], ctypes.c_char_p),
             "qlora_levels": ([i32, ctypes.POINTER(ctypes.c_float)], i32),
+            "qlora_adamw_step": ([vp, vp, vp, vp, vp, i64, ctypes.POINTER(_AdamWParams), vp], i32),
             "qlora_quantize_4bit": ([vp, i64, i32, i32, vp, vp, vp, vp], i32),
             "qlora_dequant_4bit": ([vp, vp, vp, i64, i32, i32, i32, vp, vp], i32),
             "qlora_4bit_matmul": ([ctypes.POINTER(_Weight4bit), vp, i64, i32, vp, vp], i32),
@@ -376,3 +390,28 @@ class LoRALinear4bitFunction(torch.autograd.Function):
 # the general-format entry points have the same wrappers (dispatch on the weight)
 qlora_linear_fwd_4bit = qlora_linear_fwd
 qlora_linear_bwd_4bit = qlora_linear_bwd
+
+
+def qlora_adamw_step(p32, grad, m, v, step, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                     weight_decay=0.0, p16=None):
+    """One AdamW step in place on float32 master weights ``p32`` with moments ``m``, ``v``
+    (float32) and a bf16 gradient; ``p16`` (bf16) receives the updated weights if given.
+
+    Every tensor may live on the GPU or in pinned host memory (``pin_memory=True``);
+    the work runs on the current stream of the GPU that holds ``grad`` (or GPU 0).
+    """
+    for t, dt, name in ((p32, torch.float32, "p32"), (grad, torch.bfloat16, "grad"),
+                        (m, torch.float32, "m"), (v, torch.float32, "v")):
+        if not isinstance(t, torch.Tensor) or t.dtype != dt or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous {dt} tensor")
+        if not (t.is_cuda or t.is_pinned()):
+            raise TypeError(f"{name} must be a GPU tensor or pinned host memory")
+    n = p32.numel()
+    if grad.numel() != n or m.numel() != n or v.numel() != n or (p16 is not None and p16.numel() != n):
+        raise ValueError("size mismatch")
+    if p16 is not None and (p16.dtype != torch.bfloat16 or not p16.is_contiguous()):
+        raise TypeError("p16 must be a contiguous bfloat16 tensor")
+    dev = next((t.device for t in (grad, p32, m, v) if t.is_cuda), torch.device("cuda", 0))
+    h = _AdamWParams(lr, beta1, beta2, eps, weight_decay, int(step))
+    _check(load_library().qlora_adamw_step(_ptr(p32), _ptr(p16), _ptr(grad), _ptr(m), _ptr(v), n,
+                                           ctypes.byref(h), _stream(dev)))

@@ -135,6 +135,27 @@ int check_linear(const WView& W, const void* X, const void* A, const void* B,
   return QLORA_OK;
 }
 
+// Device-usable address of an array: device memory as is, pinned host
+// memory through its device mapping. Returns false for pageable or managed
+// memory (and clears the error an unknown pointer leaves behind).
+bool device_address(const void* p, void** out) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (at.type == hipMemoryTypeDevice) {
+    *out = const_cast<void*>(p);
+    return true;
+  }
+  if (at.type == hipMemoryTypeHost && at.devicePointer) {
+    const char* base = static_cast<const char*>(at.hostPointer ? at.hostPointer : p);
+    *out = static_cast<char*>(at.devicePointer) + (static_cast<const char*>(p) - base);
+    return true;
+  }
+  return false;
+}
+
 #define QLORA_TRY(expr)                                \
   do {                                                 \
     if ((expr) != hipSuccess) return QLORA_ERR_DEVICE; \
@@ -423,6 +444,40 @@ int qlora_4bit_matmul(const qlora_4bit_weight* W, const void* act, int64_t M, in
   WView v;
   const int st = view_4bit(W, v);
   return st != QLORA_OK ? st : matmul_impl(v, act, M, transposed, out, stream);
+}
+
+int qlora_adamw_step(float* param_f32, void* param_bf16, const void* grad_bf16, float* m, float* v,
+                     int64_t n, const qlora_adamw_params* h, void* stream) {
+  if (!param_f32 || !grad_bf16 || !m || !v || !h) return QLORA_ERR_NULL;
+  if (n < 1) return QLORA_ERR_SHAPE;
+  if (!aligned(param_f32, 16) || !aligned(grad_bf16, 16) || !aligned(m, 16) || !aligned(v, 16) ||
+      (param_bf16 && !aligned(param_bf16, 16)))
+    return QLORA_ERR_ALIGN;
+  const bool ok = std::isfinite(h->lr) && h->lr >= 0.0f && h->beta1 >= 0.0f && h->beta1 < 1.0f &&
+                  h->beta2 >= 0.0f && h->beta2 < 1.0f && std::isfinite(h->eps) && h->eps > 0.0f &&
+                  std::isfinite(h->weight_decay) && h->weight_decay >= 0.0f && h->step >= 1;
+  if (!ok) return QLORA_ERR_UNSUPPORTED;
+  try {
+    void *dp = nullptr, *dp16 = nullptr, *dg = nullptr, *dm = nullptr, *dv = nullptr;
+    if (!device_address(param_f32, &dp) || !device_address(grad_bf16, &dg) || !device_address(m, &dm) ||
+        !device_address(v, &dv) || (param_bf16 && !device_address(param_bf16, &dp16)))
+      return QLORA_ERR_UNSUPPORTED;
+    AdamW a;
+    a.lr = h->lr;
+    a.beta1 = h->beta1;
+    a.beta2 = h->beta2;
+    a.one_minus_beta1 = (float)(1.0 - (double)h->beta1);
+    a.one_minus_beta2 = (float)(1.0 - (double)h->beta2);
+    a.eps = h->eps;
+    a.weight_decay = h->weight_decay;
+    a.bc1 = (float)(1.0 / (1.0 - std::pow((double)h->beta1, (double)h->step)));
+    a.bc2 = (float)(1.0 / (1.0 - std::pow((double)h->beta2, (double)h->step)));
+    QLORA_TRY(launch_adamw(static_cast<float*>(dp), static_cast<uint16_t*>(dp16), static_cast<const uint16_t*>(dg),
+                           static_cast<float*>(dm), static_cast<float*>(dv), n, a, (hipStream_t)stream));
+    return QLORA_OK;
+  } catch (...) {
+    return QLORA_ERR_DEVICE;
+  }
 }
 
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {

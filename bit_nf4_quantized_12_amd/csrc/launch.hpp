@@ -51,4 +51,11 @@ hipError_t launch_gemv(const uint16_t* X, const uint8_t* codes, const uint8_t* c
                        const float* absmax, int codebook, int N, int K, int M, const float* tpart, int tsplit,
                        int rp, const uint16_t* B, int r, float scale, uint16_t* Y, float* T_out, hipStream_t s);
 
+// AdamW step (optim.hip): bc1 = 1 / (1 - beta1^t), bc2 = 1 / (1 - beta2^t).
+struct AdamW {
+  float lr, beta1, beta2, one_minus_beta1, one_minus_beta2, eps, weight_decay, bc1, bc2;
+};
+hipError_t launch_adamw(float* p, uint16_t* p16, const uint16_t* g, float* m, float* v, int64_t n,
+                        const AdamW& a, hipStream_t s);
+
 }  // namespace qlora

@@ -219,6 +219,43 @@ int qlora_linear_bwd_4bit(const qlora_4bit_weight* W, const void* X, const void*
                           int64_t M, int64_t r, float scale, void* dX, void* dA,
                           void* dB, void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Optimizer step of the adapters, with paged optimizer state.
+ *
+ * [P1] "Paged Optimizers" and [P2] Introduction, contribution (3): optimizer
+ * state may be moved to CPU memory while GPU memory is short. The pages name
+ * no update rule; the library implements AdamW (a reading): per parameter,
+ *   m <- beta1 m + (1 - beta1) g;   v <- beta2 v + (1 - beta2) g^2
+ *   p <- p - lr (weight_decay p + m_hat / (sqrt(v_hat) + eps)),
+ *   m_hat = m / (1 - beta1^step),   v_hat = v / (1 - beta2^step)
+ * in float32 (each operation rounded to nearest), with g the bf16 gradient
+ * as qlora_linear_bwd writes it (dA, dB).
+ * "Paged": every array may be device memory or pinned host memory
+ * (hipHostMalloc); the kernel then reads and writes the host copy in place
+ * over the host link, so optimizer state paged out to the host needs no copy
+ * back before a step. Pageable (unregistered) and managed memory are
+ * refused (QLORA_ERR_UNSUPPORTED): this GPU configuration does not take page
+ * faults, so nothing migrates on demand.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  float lr;           /* >= 0 */
+  float beta1;        /* in [0, 1) */
+  float beta2;        /* in [0, 1) */
+  float eps;          /* > 0 */
+  float weight_decay; /* >= 0 */
+  int64_t step;       /* 1 for the first step */
+} qlora_adamw_params;
+
+/* One AdamW step over n parameters, in place.
+ * param_f32: float32 master weights [n] (updated). param_bf16: bf16 [n]
+ * receiving bf16(updated weight) for the next forward, or NULL. grad_bf16:
+ * bf16 gradient [n]. m, v: float32 moments [n] (updated; zero before step
+ * 1). All 16-byte aligned; device or pinned host memory; the arrays must not
+ * overlap. Errors: NULL, SHAPE (n < 1), ALIGN, UNSUPPORTED (a parameter out of
+ * range, or memory that is neither device nor pinned host), DEVICE. */
+int qlora_adamw_step(float* param_f32, void* param_bf16, const void* grad_bf16, float* m,
+                     float* v, int64_t n, const qlora_adamw_params* h, void* stream);
+
 /* Static text for a status code ("unknown status" for other values). */
 const char* qlora_status_string(int status);
 

@@ -196,3 +196,19 @@ def test_linear_4bit_validation(lib):
     assert mm(ctypes.byref(_w4(64, 64, codebook=3)), FAKE, 16, 0, FAKE, None) == UNSUPPORTED
     assert mm(ctypes.byref(_w4(64, 64)), FAKE, 16, 2, FAKE, None) == UNSUPPORTED
     assert mm(ctypes.byref(_w4(64, 64)), FAKE, 0, 0, FAKE, None) == SHAPE
+
+
+def test_adamw_validation(lib):
+    f = lib.qlora_adamw_step
+    good = q._AdamWParams(1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    h = ctypes.byref(good)
+    assert f(None, None, FAKE, FAKE, FAKE, 64, h, None) == NULL
+    assert f(FAKE, None, FAKE, FAKE, FAKE, 64, None, None) == NULL
+    assert f(FAKE, None, FAKE, FAKE, FAKE, 0, h, None) == SHAPE
+    assert f(FAKE + 4, None, FAKE, FAKE, FAKE, 64, h, None) == ALIGN
+    assert f(FAKE, FAKE + 2, FAKE, FAKE, FAKE, 64, h, None) == ALIGN
+    for bad in (q._AdamWParams(-1.0, 0.9, 0.999, 1e-8, 0.0, 1), q._AdamWParams(1e-3, 1.0, 0.999, 1e-8, 0.0, 1),
+                q._AdamWParams(1e-3, 0.9, 1.5, 1e-8, 0.0, 1), q._AdamWParams(1e-3, 0.9, 0.999, 0.0, 0.0, 1),
+                q._AdamWParams(1e-3, 0.9, 0.999, 1e-8, -0.1, 1), q._AdamWParams(1e-3, 0.9, 0.999, 1e-8, 0.0, 0),
+                q._AdamWParams(float("nan"), 0.9, 0.999, 1e-8, 0.0, 1)):
+        assert f(FAKE, None, FAKE, FAKE, FAKE, 64, ctypes.byref(bad), None) == UNSUPPORTED
