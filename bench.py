@@ -27,6 +27,10 @@ Legs timed in the same run (HBM-bound rows of the path):
             one 22016x8192 weight (each format's own bytes per weight), the
             relative dequantisation error on N(0, 0.02) weights, bits per
             weight, and the forward GEMM at 8192x4096x4096
+  adamw     the adapters' optimizer step for a 32-layer 7B model (160M LoRA
+            parameters, 28 B moved per parameter) with the moments in HBM,
+            then paged out to pinned host memory (the kernel works on them
+            in place over the host link), and the page-out / page-in copies
   copycal   one elementwise pass reading and writing exactly 1 GiB each, the
             calibration point of those counters
             (see bit_nf4_quantized_12_amd/pmc_traffic.py)
@@ -58,7 +62,7 @@ def parse():
     ap.add_argument("--config", choices=["7b", "65b"], default="7b",
                     help="layer shapes of the step: LLaMA-7B (default) or 65B-class")
     ap.add_argument("--stack-layers", type=int, default=80, help="65B-class layers in the quantize leg")
-    ap.add_argument("--legs", default="roofline,quantize,gemv,gemm512,formats",
+    ap.add_argument("--legs", default="roofline,quantize,gemv,gemm512,formats,adamw",
                     help="comma list of extra legs, or 'none'")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -322,6 +326,56 @@ def main():
                 del W, Wg
         legs["formats_22016x8192"] = fmt
         del w, wf, Xg, wg, og
+        torch.cuda.empty_cache()
+
+    # ---- the adapters' optimizer step, state in HBM or paged out to pinned host memory -------
+    if "adamw" in want:
+        per_layer = sum(r * (K + N) for _, N, K in synth.llama_linears(4096, 11008))
+        n_opt = 32 * per_layer  # the LoRA parameters of a 32-layer 7B model
+        p32 = torch.zeros(n_opt, dtype=torch.float32, device=dev)
+        p16 = torch.empty(n_opt, dtype=torch.bfloat16, device=dev)
+        g = synth.device_normal_bf16(n_opt, 1e-3, 3_000_001, dev)
+        m_d = torch.zeros(n_opt, dtype=torch.float32, device=dev)
+        v_d = torch.zeros(n_opt, dtype=torch.float32, device=dev)
+        byts = 28.0 * n_opt  # p32 r/w, m r/w, v r/w, bf16 grad, bf16 copy
+        q.qlora_adamw_step(p32, g, m_d, v_d, 1, p16=p16)
+        stepno = [1]
+
+        def opt_dev():
+            stepno[0] += 1
+            q.qlora_adamw_step(p32, g, m_d, v_d, stepno[0], p16=p16)
+
+        td = timed(opt_dev, 5) / 5
+        m_h = torch.zeros(n_opt, dtype=torch.float32).pin_memory()
+        v_h = torch.zeros(n_opt, dtype=torch.float32).pin_memory()
+
+        def page_out():
+            m_h.copy_(m_d, non_blocking=True)
+            v_h.copy_(v_d, non_blocking=True)
+
+        def page_in():
+            m_d.copy_(m_h, non_blocking=True)
+            v_d.copy_(v_h, non_blocking=True)
+
+        tout = timed(page_out, 2) / 2
+        tin = timed(page_in, 2) / 2
+
+        def opt_host():
+            stepno[0] += 1
+            q.qlora_adamw_step(p32, g, m_h, v_h, stepno[0], p16=p16)
+
+        opt_host()
+        th = timed(opt_host, 2) / 2
+        legs["adamw_7b_adapters"] = {
+            "params": n_opt, "bytes_per_param": 28,
+            "state_in_hbm_ms": round(td * 1e3, 3), "state_in_hbm_GB/s": round(byts / td / 1e9, 1),
+            "state_in_hbm_hbm_frac": round(byts / td / 1e9 / PEAK_HBM_GBS, 4),
+            "state_in_pinned_host_ms": round(th * 1e3, 3),
+            "state_in_pinned_host_link_GB/s": round(16.0 * n_opt / th / 1e9, 1),
+            "page_out_ms": round(tout * 1e3, 3), "page_in_ms": round(tin * 1e3, 3),
+            "page_GB/s": round(8.0 * n_opt / ((tout + tin) / 2) / 1e9, 1)}
+        log(f"adamw: {legs['adamw_7b_adapters']}")
+        del p32, p16, g, m_d, v_d, m_h, v_h
         torch.cuda.empty_cache()
 
     # ---- CPU oracle on a bounded sample of the step ---------------------------------------
