@@ -40,5 +40,7 @@ from .nf4_oracle import (  # noqa: F401
     storage_bits_per_param,
     linear_fwd,
     linear_bwd,
+    grouped_linear_fwd,
+    grouped_linear_bwd,
 )
 from .adamw import adamw_step  # noqa: F401

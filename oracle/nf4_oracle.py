@@ -397,3 +397,35 @@ def linear_bwd(X, W, A, B, dY, s, need_dX=True):
     dA = s * (U.T @ X)
     dB = s * (dY.T @ T)
     return dX, dA, dB
+
+
+def grouped_linear_fwd(X, W, A, B, s, groups):
+    """Linears that share the input X (q / k / v of a decoder layer).
+
+    W [g Ns, K], A [g r, K] and B [g Ns, r] stack the segments; segment i is
+    linear_fwd(X, W_i, A_i, B_i, s). Returns (Y [M, g Ns], T [M, g r]).
+    """
+    W, A, B = (np.asarray(t, dtype=np.float64) for t in (W, A, B))
+    g = int(groups)
+    ns, r = W.shape[0] // g, A.shape[0] // g
+    outs = [linear_fwd(X, W[i * ns:(i + 1) * ns], A[i * r:(i + 1) * r], B[i * ns:(i + 1) * ns], s)
+            for i in range(g)]
+    return np.concatenate([o[0] for o in outs], axis=1), np.concatenate([o[1] for o in outs], axis=1)
+
+
+def grouped_linear_bwd(X, W, A, B, dY, s, groups, need_dX=True):
+    """Backward of grouped_linear_fwd: dX summed over the segments (they share
+    X), dA [g r, K] and dB [g Ns, r] stacked like A and B."""
+    A, B, dY = (np.asarray(t, dtype=np.float64) for t in (A, B, dY))
+    g = int(groups)
+    ns, r = B.shape[0] // g, A.shape[0] // g
+    dX, dA, dB = None, [], []
+    for i in range(g):
+        Wi = None if W is None else np.asarray(W, dtype=np.float64)[i * ns:(i + 1) * ns]
+        dXi, dAi, dBi = linear_bwd(X, Wi, A[i * r:(i + 1) * r], B[i * ns:(i + 1) * ns],
+                                   dY[:, i * ns:(i + 1) * ns], s, need_dX=need_dX)
+        if need_dX:
+            dX = dXi if dX is None else dX + dXi
+        dA.append(dAi)
+        dB.append(dBi)
+    return dX, np.concatenate(dA, axis=0), np.concatenate(dB, axis=0)
