@@ -14,6 +14,8 @@ The function names are those of the C ABI (include/qlora.h):
 * ``qlora_linear_workspace_bytes(M, N, K, r)``
 * ``qlora_linear_fwd(W, X, A, B, scale, ...)``
 * ``qlora_linear_bwd(W, X, A, B, dY, T, scale, ...)``
+* ``qlora_linear_fwd_grouped`` / ``qlora_linear_bwd_grouped``: linears that share
+  one input (q / k / v, gate / up), weights and adapters stacked by segment
 * ``qlora_adamw_step(p32, grad, m, v, step, ...)``: the adapters' optimizer
   step; the state may sit in HBM or in pinned host memory (paged out)
 * ``qlora_levels(codebook)``, ``qlora_quantize_4bit(w, codebook, double_quant)``,
@@ -101,6 +103,9 @@ def load_library(path=LIB_PATH):
             "qlora_status_string": ([i32], ctypes.c_char_p),
             "qlora_levels": ([i32, ctypes.POINTER(ctypes.c_float)], i32),
             "qlora_adamw_step": ([vp, vp, vp, vp, vp, i64, ctypes.POINTER(_AdamWParams), vp], i32),
+            "qlora_linear_grouped_workspace_bytes": ([i64, i64, i64, i64, i64], sz),
+            "qlora_linear_fwd_grouped": ([ctypes.POINTER(_Weight4bit), i64, vp, vp, vp, i64, i64, f32, vp, vp, vp, sz, vp], i32),
+            "qlora_linear_bwd_grouped": ([ctypes.POINTER(_Weight4bit), i64, vp, vp, vp, vp, vp, i64, i64, f32, vp, vp, vp, vp, sz, vp], i32),
             "qlora_quantize_4bit": ([vp, i64, i32, i32, vp, vp, vp, vp], i32),
             "qlora_dequant_4bit": ([vp, vp, vp, i64, i32, i32, i32, vp, vp], i32),
             "qlora_4bit_matmul": ([ctypes.POINTER(_Weight4bit), vp, i64, i32, vp, vp], i32),
@@ -415,3 +420,80 @@ def qlora_adamw_step(p32, grad, m, v, step, lr=1e-3, beta1=0.9, beta2=0.999, eps
     h = _AdamWParams(lr, beta1, beta2, eps, weight_decay, int(step))
     _check(load_library().qlora_adamw_step(_ptr(p32), _ptr(p16), _ptr(grad), _ptr(m), _ptr(v), n,
                                            ctypes.byref(h), _stream(dev)))
+
+
+def _weight4_struct(W):
+    """The general 4-bit weight struct for any stored format (grouped entry points)."""
+    _need(W.codes, torch.uint8, "W.codes")
+    _need(W.c2, torch.uint8 if W.double_quant else torch.float32, "W.c2")
+    if W.double_quant:
+        _need(W.c1, torch.float32, "W.c1")
+    c1 = W.c1.data_ptr() if W.double_quant else None
+    return _Weight4bit(W.codes.data_ptr(), W.c2.data_ptr(), c1, W.rows, W.cols, _codebook_id(W.codebook),
+                       1 if W.double_quant else 0)
+
+
+def qlora_linear_grouped_workspace_bytes(M, N, K, r, groups):
+    return int(load_library().qlora_linear_grouped_workspace_bytes(M, N, K, r, groups))
+
+
+def qlora_linear_fwd_grouped(W, groups, X, A, B, scale, save_T=True, Y=None, T=None, workspace=None):
+    """Grouped forward: W [g Ns, K] stacked weights, A [g r, K], B [g Ns, r].
+
+    Returns (Y [M, g Ns] bf16, T [M, g r] float32 or None).
+    """
+    _need(X, torch.bfloat16, "X")
+    _need(A, torch.bfloat16, "A")
+    _need(B, torch.bfloat16, "B")
+    M, K = X.shape
+    g = int(groups)
+    r = A.shape[0] // g
+    if A.shape != (g * r, K) or B.shape != (W.rows, r) or W.cols != K:
+        raise ValueError("shape mismatch: X [M, K], A [g r, K], B [g Ns, r], W [g Ns, K]")
+    dev = X.device
+    if Y is None:
+        Y = torch.empty((M, W.rows), dtype=torch.bfloat16, device=dev)
+    if save_T and T is None:
+        T = torch.empty((M, g * r), dtype=torch.float32, device=dev)
+    if not save_T:
+        T = None
+    need = qlora_linear_grouped_workspace_bytes(M, W.rows, K, r, g)
+    ws = workspace if workspace is not None and workspace.numel() >= need else \
+        torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    w = _weight4_struct(W)
+    _check(load_library().qlora_linear_fwd_grouped(ctypes.byref(w), g, _ptr(X), _ptr(A), _ptr(B), M, r,
+                                                   float(scale), _ptr(Y), _ptr(T), _ptr(ws), ws.numel(),
+                                                   _stream(dev)))
+    return Y, T
+
+
+def qlora_linear_bwd_grouped(W, groups, X, A, B, dY, T, scale, need_dX=True, dX=None, dA=None, dB=None,
+                             workspace=None):
+    """Grouped backward: (dX [M, K] summed over the segments or None, dA [g r, K], dB [g Ns, r])."""
+    for t, name in ((X, "X"), (A, "A"), (B, "B"), (dY, "dY")):
+        _need(t, torch.bfloat16, name)
+    if T is not None:
+        _need(T, torch.float32, "T")
+    M, K = X.shape
+    g = int(groups)
+    r = A.shape[0] // g
+    N = W.rows
+    if dY.shape != (M, N) or A.shape != (g * r, K) or B.shape != (N, r) or W.cols != K:
+        raise ValueError("shape mismatch")
+    dev = X.device
+    if need_dX and dX is None:
+        dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    if not need_dX:
+        dX = None
+    if dA is None:
+        dA = torch.empty((g * r, K), dtype=torch.bfloat16, device=dev)
+    if dB is None:
+        dB = torch.empty((N, r), dtype=torch.bfloat16, device=dev)
+    need = qlora_linear_grouped_workspace_bytes(M, N, K, r, g)
+    ws = workspace if workspace is not None and workspace.numel() >= need else \
+        torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    w = _weight4_struct(W)
+    _check(load_library().qlora_linear_bwd_grouped(ctypes.byref(w), g, _ptr(X), _ptr(A), _ptr(B), _ptr(dY),
+                                                   _ptr(T), M, r, float(scale), _ptr(dX), _ptr(dA), _ptr(dB),
+                                                   _ptr(ws), ws.numel(), _stream(dev)))
+    return dX, dA, dB

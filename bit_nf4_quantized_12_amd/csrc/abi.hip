@@ -181,6 +181,8 @@ int matmul_impl(const WView& W, const void* act, int64_t M, int transposed, void
     p.lora_l = nullptr;
     p.lora_r = nullptr;
     p.rp = 0;
+    p.lora_ld = 0;
+    p.lora_seg = 0;
     p.out = static_cast<uint16_t*>(out);
     p.M = (int)M;
     p.Nout = (int)(transposed ? K : N);
@@ -242,6 +244,8 @@ int fwd_impl(const WView& W, const void* X, const void* A, const void* B, int64_
     p.lora_l = Ts;
     p.lora_r = Br;
     p.rp = rp;
+    p.lora_ld = rp;
+    p.lora_seg = 0;
     p.out = static_cast<uint16_t*>(Y);
     p.M = (int)M;
     p.Nout = (int)N;
@@ -302,7 +306,7 @@ int bwd_impl(const WView& W, const void* X, const void* A, const void* B, const 
     }
     // U = dY B: B^T [r, N] is the row operand of the projection; A^T [K, rp]
     // is the column operand of the dX epilogue (one launch for both)
-    QLORA_TRY(launch_transpose2(Bh, Ah, (int)N, (int)K, (int)r, rp, Bt, dX ? At : nullptr, s));
+    QLORA_TRY(launch_transpose2(Bh, Ah, (int)N, (int)K, (int)r, (int)r, rp, Bt, dX ? At : nullptr, s));
     QLORA_TRY(launch_proj(dYh, Bt, (int)M, (int)N, (int)r, rp, L.usplit, partU, s));
     if (streamed_dB)
       QLORA_TRY(launch_finalize2(partU, L.usplit, (int)M, Mp, (int)r, rp, scale, U32, PtH, PtL, T, TtH, TtL, s));
@@ -322,6 +326,8 @@ int bwd_impl(const WView& W, const void* X, const void* A, const void* B, const 
       p.lora_l = PtH;
       p.lora_r = At;
       p.rp = rp;
+      p.lora_ld = rp;
+      p.lora_seg = 0;
       p.out = static_cast<uint16_t*>(dX);
       p.M = (int)M;
       p.Nout = (int)K;
@@ -335,12 +341,167 @@ int bwd_impl(const WView& W, const void* X, const void* A, const void* B, const 
     if (streamed_dB) {
       QLORA_TRY(launch_grad_tr(TtH, TtL, dYh, (int)M, Mp, (int)N, rp, L.sB, true, gpartB, s));
       QLORA_TRY(launch_grad_reduce2(gpartA, L.sA, (int)K, static_cast<uint16_t*>(dA), gpartB, L.sB, (int)N,
-                                    static_cast<uint16_t*>(dB), (int)r, rp, 1.0f, s));
+                                    static_cast<uint16_t*>(dB), (int)r, rp, (int)r, rp, 1.0f, s));
     } else {
       QLORA_TRY(launch_grad_reduce(gpartA, L.sA, (int)r, rp, (int)K, 1.0f, false, false, static_cast<uint16_t*>(dA), s));
       QLORA_TRY(launch_grad(T, dYh, (int)M, (int)N, (int)r, rp, L.sB, gpartB, s));
       QLORA_TRY(launch_grad_reduce(gpartB, L.sB, (int)r, rp, (int)N, scale, true, false, static_cast<uint16_t*>(dB), s));
     }
+    return QLORA_OK;
+  } catch (...) {
+    return QLORA_ERR_DEVICE;
+  }
+}
+
+
+// ---- grouped linears: g segments of output columns sharing one input ---------------------
+// W is [g Ns, K] (the segments' weights stacked), A [g r, K], B [g Ns, r];
+// segment i computes Y_i = X W_i~^T + s (X A_i^T) B_i^T, and the backward
+// sums dX over the segments. Needs Ns % 256 == 0 (no GEMM tile straddles two
+// segments) and r % 64 == 0 (each segment's rank is whole 64-column blocks).
+int check_grouped(const WView& W, int64_t g, int64_t r) {
+  if (g < 1 || g > 16) return QLORA_ERR_SHAPE;
+  if (g == 1) return QLORA_OK;
+  if (W.N % g != 0 || (W.N / g) % 256 != 0 || r % 64 != 0) return QLORA_ERR_SHAPE;
+  return QLORA_OK;
+}
+
+int fwd_grouped_impl(const WView& W, int64_t g, const void* X, const void* A, const void* B, int64_t M, int64_t r,
+                     float scale, void* Y, float* T_save, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_grouped(W, g, r);
+  if (st != QLORA_OK) return st;
+  if (g == 1) return fwd_impl(W, X, A, B, M, r, scale, Y, T_save, ws, ws_bytes, stream);
+  const int64_t R = g * r;
+  st = check_linear(W, X, A, B, M, r, scale, ws, ws_bytes);
+  if (st != QLORA_OK) return st;
+  if (!Y) return QLORA_ERR_NULL;
+  if (!aligned(Y, 16) || (T_save && !aligned(T_save, 4))) return QLORA_ERR_ALIGN;
+  const int64_t N = W.N, K = W.K, Ns = N / g;
+  const Layout L = plan(M, N, K, R);
+  if (ws_bytes < L.fwd_total) return QLORA_ERR_WORKSPACE;
+  try {
+    if (tables_status() != 0) return QLORA_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    char* base = static_cast<char*>(ws);
+    float* partT = reinterpret_cast<float*>(base + L.partT);
+    float* T32 = T_save ? T_save : reinterpret_cast<float*>(base + L.T32);
+    uint16_t* Ts = reinterpret_cast<uint16_t*>(base + L.Ts);
+    const uint16_t* Xh = static_cast<const uint16_t*>(X);
+    const uint16_t* Ah = static_cast<const uint16_t*>(A);
+    const uint16_t* Bh = static_cast<const uint16_t*>(B);
+    // T = X [A_1; ..; A_g]^T: one pass over X for all segments
+    QLORA_TRY(launch_proj_seg(Xh, K, 0, Ah, K, 0, (int)(R / 64), (int)M, (int)K, (int)R, (int)R, L.tsplit, partT, s));
+    if (M <= kGemvMaxM) {
+      QLORA_TRY(launch_gemv(Xh, W.codes, W.c2, W.c1, W.absmax, W.cb, (int)N, (int)K, (int)M, partT, L.tsplit,
+                            (int)R, Bh, (int)r, scale, static_cast<uint16_t*>(Y), T_save, s, (int)Ns, (int)R));
+      return QLORA_OK;
+    }
+    QLORA_TRY(launch_finalize(partT, L.tsplit, (int)M, (int)M, (int)R, (int)R, scale, T32, Ts, nullptr, s));
+    GemmParams p;
+    p.act = Xh;
+    p.codes = W.codes;
+    p.c2 = W.c2;
+    p.c1 = W.c1;
+    p.absmax = W.absmax;
+    p.wN = N;
+    p.wK = K;
+    p.lora_l = Ts;
+    p.lora_r = Bh;
+    p.rp = (int)r;
+    p.lora_ld = (int)R;
+    p.lora_seg = (int)Ns;
+    p.out = static_cast<uint16_t*>(Y);
+    p.M = (int)M;
+    p.Nout = (int)N;
+    p.Kred = (int)K;
+    p.lv = host_levels(W.cb);
+    QLORA_TRY(launch_gemm(p, false, s));
+    return QLORA_OK;
+  } catch (...) {
+    return QLORA_ERR_DEVICE;
+  }
+}
+
+int bwd_grouped_impl(const WView& W, int64_t g, const void* X, const void* A, const void* B, const void* dY,
+                     const float* T_saved, int64_t M, int64_t r, float scale, void* dX, void* dA, void* dB,
+                     void* ws, size_t ws_bytes, void* stream) {
+  int st = check_grouped(W, g, r);
+  if (st != QLORA_OK) return st;
+  if (g == 1) return bwd_impl(W, X, A, B, dY, T_saved, M, r, scale, dX, dA, dB, ws, ws_bytes, stream);
+  const int64_t R = g * r;
+  st = check_linear(W, X, A, B, M, r, scale, ws, ws_bytes);
+  if (st != QLORA_OK) return st;
+  if (!dY || !dA || !dB) return QLORA_ERR_NULL;
+  if (!aligned(dY, 16) || !aligned(dA, 16) || !aligned(dB, 16) || (dX && !aligned(dX, 16)) ||
+      (T_saved && !aligned(T_saved, 4)))
+    return QLORA_ERR_ALIGN;
+  const int64_t N = W.N, K = W.K, Ns = N / g;
+  const Layout L = plan(M, N, K, R);
+  if (ws_bytes < L.bwd_total) return QLORA_ERR_WORKSPACE;
+  try {
+    if (tables_status() != 0) return QLORA_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    char* base = static_cast<char*>(ws);
+    const uint16_t* Xh = static_cast<const uint16_t*>(X);
+    const uint16_t* Ah = static_cast<const uint16_t*>(A);
+    const uint16_t* Bh = static_cast<const uint16_t*>(B);
+    const uint16_t* dYh = static_cast<const uint16_t*>(dY);
+    uint16_t* Bt = reinterpret_cast<uint16_t*>(base + L.Bt);
+    uint16_t* At = reinterpret_cast<uint16_t*>(base + L.At);
+    float* partU = reinterpret_cast<float*>(base + L.partU);
+    float* U32 = reinterpret_cast<float*>(base + L.U32);
+    const int Mp = (int)(cdiv(M, 64) * 64);
+    uint16_t* PtH = reinterpret_cast<uint16_t*>(base + L.PtH);
+    uint16_t* PtL = reinterpret_cast<uint16_t*>(base + L.PtL);
+    uint16_t* TtH = reinterpret_cast<uint16_t*>(base + L.TtH);
+    uint16_t* TtL = reinterpret_cast<uint16_t*>(base + L.TtL);
+    float* gpartA = reinterpret_cast<float*>(base + L.gpartA);
+    float* gpartB = reinterpret_cast<float*>(base + L.gpartB);
+    const float* T = T_saved;
+    if (!T) {
+      float* partT = reinterpret_cast<float*>(base + L.partT);
+      float* T32 = reinterpret_cast<float*>(base + L.T32);
+      uint16_t* Ts = reinterpret_cast<uint16_t*>(base + L.Ts);
+      QLORA_TRY(launch_proj_seg(Xh, K, 0, Ah, K, 0, (int)(R / 64), (int)M, (int)K, (int)R, (int)R, L.tsplit, partT,
+                                s));
+      QLORA_TRY(launch_finalize(partT, L.tsplit, (int)M, (int)M, (int)R, (int)R, 1.0f, T32, Ts, nullptr, s));
+      T = T32;
+    }
+    // B^T [r, N] (segment i in columns i Ns ..) and [A_1; ..; A_g]^T [K, R]
+    QLORA_TRY(launch_transpose2(Bh, Ah, (int)N, (int)K, (int)r, (int)R, (int)R, Bt, dX ? At : nullptr, s));
+    // U_i = dY_i B_i: segment i reads dY and B^T at column offset i Ns
+    const int usplit = proj_splits(M, Ns);
+    QLORA_TRY(launch_proj_seg(dYh, N, Ns, Bt, N, Ns, (int)(r / 64), (int)M, (int)Ns, (int)r, (int)R, usplit, partU,
+                              s));
+    QLORA_TRY(launch_finalize2(partU, usplit, (int)M, Mp, (int)R, (int)R, scale, U32, PtH, PtL, T, TtH, TtL, s));
+    if (dX) {
+      // dX = sum_i (dY_i W_i~ + (s U_i) A_i) = dY W~ + (s U) [A_1; ..; A_g]
+      GemmParams p;
+      p.act = dYh;
+      p.codes = W.codes;
+      p.c2 = W.c2;
+      p.c1 = W.c1;
+      p.absmax = W.absmax;
+      p.wN = N;
+      p.wK = K;
+      p.lora_l = PtH;
+      p.lora_r = At;
+      p.rp = (int)R;
+      p.lora_ld = (int)R;
+      p.lora_seg = 0;
+      p.out = static_cast<uint16_t*>(dX);
+      p.M = (int)M;
+      p.Nout = (int)K;
+      p.Kred = (int)N;
+      p.lv = host_levels(W.cb);
+      QLORA_TRY(launch_gemm(p, true, s));
+    }
+    // dA_i = (s U_i)^T X for all segments in one pass over X; dB_i from dY_i
+    // and segment i's columns of s T only
+    QLORA_TRY(launch_grad_tr(PtH, PtL, Xh, (int)M, Mp, (int)K, (int)R, L.sA, false, gpartA, s));
+    QLORA_TRY(launch_grad_tr(TtH, TtL, dYh, (int)M, Mp, (int)N, (int)R, L.sB, true, gpartB, s, (int)Ns, (int)r));
+    QLORA_TRY(launch_grad_reduce2(gpartA, L.sA, (int)K, static_cast<uint16_t*>(dA), gpartB, L.sB, (int)N,
+                                  static_cast<uint16_t*>(dB), (int)R, (int)R, (int)r, (int)r, 1.0f, s));
     return QLORA_OK;
   } catch (...) {
     return QLORA_ERR_DEVICE;
@@ -478,6 +639,32 @@ int qlora_adamw_step(float* param_f32, void* param_bf16, const void* grad_bf16, 
   } catch (...) {
     return QLORA_ERR_DEVICE;
   }
+}
+
+size_t qlora_linear_grouped_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r, int64_t groups) {
+  if (groups < 1 || groups > 16 || M < 1 || N < 1 || K < 64 || (K % 64) != 0 || r < 1 || r > 256) return 0;
+  if (groups > 1 && (N % groups != 0 || (N / groups) % 256 != 0 || r % 64 != 0)) return 0;
+  if (M * std::max(N, K) >= (int64_t(1) << 31)) return 0;
+  const Layout L = plan(M, N, K, groups * r);
+  return std::max(L.fwd_total, L.bwd_total);
+}
+
+int qlora_linear_fwd_grouped(const qlora_4bit_weight* W, int64_t groups, const void* X, const void* A,
+                             const void* B, int64_t M, int64_t r, float scale, void* Y, float* T_save, void* ws,
+                             size_t ws_bytes, void* stream) {
+  WView v;
+  const int st = view_4bit(W, v);
+  return st != QLORA_OK ? st : fwd_grouped_impl(v, groups, X, A, B, M, r, scale, Y, T_save, ws, ws_bytes, stream);
+}
+
+int qlora_linear_bwd_grouped(const qlora_4bit_weight* W, int64_t groups, const void* X, const void* A,
+                             const void* B, const void* dY, const float* T_saved, int64_t M, int64_t r,
+                             float scale, void* dX, void* dA, void* dB, void* ws, size_t ws_bytes, void* stream) {
+  WView v;
+  const int st = view_4bit(W, v);
+  return st != QLORA_OK ? st
+                        : bwd_grouped_impl(v, groups, X, A, B, dY, T_saved, M, r, scale, dX, dA, dB, ws, ws_bytes,
+                                           stream);
 }
 
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {

@@ -325,13 +325,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
     // acc += lora_l[rows, :] lora_r[cols, :]^T, 64 rank columns per step
     // (rp is a multiple of 64, zero padded), staged through LDS stage 0 by
     // LDS-DMA like the main loop; the loop ended on a barrier.
+    // grouped linears: this tile's segment of output columns uses its own
+    // rp columns of lora_l (tiles never straddle segments)
+    const int lcol0 = p.lora_seg ? (n0 / p.lora_seg) * p.rp : 0;
     for (int kr = 0; kr < p.rp; kr += BK) {
 #pragma unroll
       for (int j = 0; j < BM / 64; ++j) {
         const int R = (BM / 8) * wu + 8 * j + (l >> 3);
         const int c = (l & 7) ^ swz(R);
         const int ra = min(m0 + R, p.M - 1);
-        __builtin_amdgcn_global_load_lds((gbl_void_t*)(p.lora_l + (int64_t)ra * p.rp + kr + 8 * c),
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(p.lora_l + (int64_t)ra * p.lora_ld + lcol0 + kr + 8 * c),
                                          (lds_void_t*)(sA + ((BM / 8) * wu + 8 * j) * 64), 16, 0, 0);
       }
 #pragma unroll

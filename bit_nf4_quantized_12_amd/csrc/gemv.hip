@@ -64,13 +64,17 @@ __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
     const float* __restrict__ c1, const float* __restrict__ absmax, int N, int K, int M,
     const float* __restrict__ tpart, int tsplit, int rp,
     const uint16_t* __restrict__ B, int r, float scale, uint16_t* __restrict__ Y, float* __restrict__ T_out,
-    Levels lv) {
+    int segN, int tld, Levels lv) {
   __shared__ float red[GV_WAVES][16][17];
   __shared__ float sT[16][257];
   __shared__ uint16_t sB[16 * 256];  // the workgroup's 16 rows of B
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n0 = blockIdx.x * 16;
+  // grouped linears: rows of segment z = n0 / segN use T columns z r .. + r
+  // (T_out [M, tld] gets them from the segment's first workgroup)
+  const int zc = segN ? (n0 / segN) * r : 0;
+  const bool t_writer = segN ? (n0 % segN) == 0 : blockIdx.x == 0;
   const int c = l & 15, g = l >> 4;
   const int n = min(n0 + c, N - 1);  // rows past N: clamped read, result not stored
   const bool xok = c < M;            // A-operand row = X row c (zero past M)
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
   const int tm = hast ? tid / r : 0, tj = hast ? tid % r : 0;
   float tp[16];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) tp[k] = (hast && k < tsplit) ? tpart[((int64_t)k * M + tm) * rp + tj] : 0.0f;
+  for (int k = 0; k < 16; ++k) tp[k] = (hast && k < tsplit) ? tpart[((int64_t)k * M + tm) * rp + zc + tj] : 0.0f;
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int ch = w; ch < nchunks; ch += 2 * GV_WAVES) {
@@ -140,9 +144,9 @@ __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
       float s = 0.0f;
 #pragma unroll
       for (int k = 0; k < 16; ++k) s += tp[k];
-      for (int k = 16; k < tsplit; ++k) s += tpart[((int64_t)k * M + tm) * rp + tj];
+      for (int k = 16; k < tsplit; ++k) s += tpart[((int64_t)k * M + tm) * rp + zc + tj];
       sT[tm][tj] = s;
-      if (blockIdx.x == 0 && T_out) T_out[(int64_t)tm * r + tj] = s;
+      if (t_writer && T_out) T_out[(int64_t)tm * tld + zc + tj] = s;
     }
   } else {
     for (int idx = tid; idx < 16 * r; idx += 64 * GV_WAVES) {
@@ -152,9 +156,9 @@ __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
     for (int idx = tid; idx < M * r; idx += 64 * GV_WAVES) {
       const int m = idx / r, j = idx % r;
       float s = 0.0f;
-      for (int k = 0; k < tsplit; ++k) s += tpart[((int64_t)k * M + m) * rp + j];
+      for (int k = 0; k < tsplit; ++k) s += tpart[((int64_t)k * M + m) * rp + zc + j];
       sT[m][j] = s;
-      if (blockIdx.x == 0 && T_out) T_out[(int64_t)m * r + j] = s;
+      if (t_writer && T_out) T_out[(int64_t)m * tld + zc + j] = s;
     }
   }
   __syncthreads();
@@ -175,13 +179,15 @@ __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
 
 hipError_t launch_gemv(const uint16_t* X, const uint8_t* codes, const uint8_t* c2, const float* c1,
                        const float* absmax, int codebook, int N, int K, int M, const float* tpart, int tsplit,
-                       int rp, const uint16_t* B, int r, float scale, uint16_t* Y, float* T_out, hipStream_t s) {
+                       int rp, const uint16_t* B, int r, float scale, uint16_t* Y, float* T_out, hipStream_t s,
+                       int segN, int tld) {
+  if (!tld) tld = r;
   if (absmax)
     hipLaunchKernelGGL(gemv_kernel<true>, dim3((N + 15) / 16), dim3(64 * GV_WAVES), 0, s, X, codes, c2, c1, absmax,
-                       N, K, M, tpart, tsplit, rp, B, r, scale, Y, T_out, host_levels(codebook));
+                       N, K, M, tpart, tsplit, rp, B, r, scale, Y, T_out, segN, tld, host_levels(codebook));
   else
     hipLaunchKernelGGL(gemv_kernel<false>, dim3((N + 15) / 16), dim3(64 * GV_WAVES), 0, s, X, codes, c2, c1, absmax,
-                       N, K, M, tpart, tsplit, rp, B, r, scale, Y, T_out, host_levels(codebook));
+                       N, K, M, tpart, tsplit, rp, B, r, scale, Y, T_out, segN, tld, host_levels(codebook));
   return hipGetLastError();
 }
 

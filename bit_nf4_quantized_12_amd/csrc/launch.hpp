@@ -12,9 +12,11 @@ struct GemmParams {
   const float* c1;
   const float* absmax;     // fp32 block constants (no double quantisation), or null
   int64_t wN, wK;
-  const uint16_t* lora_l;  // [M, rp] bf16 (scale folded in), or null
+  const uint16_t* lora_l;  // [M, lora_ld] bf16 (scale folded in), or null
   const uint16_t* lora_r;  // [Nout, rp] bf16, or null
   int rp;                  // multiple of 64, columns past r are zero
+  int lora_ld;             // row pitch of lora_l (rp, or more for grouped linears)
+  int lora_seg;            // > 0: output columns n use lora_l columns (n / lora_seg) rp .. + rp
   uint16_t* out;           // [M, Nout] bf16
   int M, Nout, Kred;
   Levels lv;
@@ -29,27 +31,39 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* c2, const float* 
 hipError_t launch_gemm(const GemmParams& p, bool transposed_w, hipStream_t s);
 hipError_t launch_proj(const uint16_t* L, const uint16_t* R, int M, int Kr, int r, int rp,
                        int nsplit, float* part, hipStream_t s);
+// Streamed projection (Kr % 64 == 0, rp_total % 64 == 0), part
+// [nsplit][M][rp_total]. The result's 64-column blocks come in segments of
+// zper blocks; segment g multiplies L + g segL by rows of R + g segR (r_seg
+// valid rows), row pitches ldL / ldR.
+hipError_t launch_proj_seg(const uint16_t* L, int64_t ldL, int64_t segL, const uint16_t* R, int64_t ldR,
+                           int64_t segR, int zper, int M, int Kr, int r_seg, int rp_total, int nsplit, float* part,
+                           hipStream_t s);
 hipError_t launch_finalize(const float* part, int nsplit, int M, int Mp, int r, int rp, float scale,
                            float* P32, uint16_t* Ph, uint16_t* Pl, hipStream_t s);
 hipError_t launch_grad(const float* P, const uint16_t* Q, int M, int C, int r, int rp, int nsplit,
                        float* part, hipStream_t s);
 hipError_t launch_grad_reduce(const float* part, int nsplit, int r, int rp, int C, float scale,
                               bool transpose, bool part_trans, uint16_t* out, hipStream_t s);
+// segC > 0: the columns of segment c / segC pair only with plane columns
+// (c / segC) rseg .. + rseg (grouped linears); the result then has rseg rows.
 hipError_t launch_grad_tr(const uint16_t* Ph, const uint16_t* Pl, const uint16_t* Q, int M, int Mp, int C,
-                          int rp, int nsplit, bool trans, float* part, hipStream_t s);
+                          int rp, int nsplit, bool trans, float* part, hipStream_t s, int segC = 0,
+                          int rseg = 0);
 hipError_t launch_relayout(const uint16_t* in, int64_t rows_in, int64_t cols_in, int64_t ldi,
                            bool transpose, uint16_t* out, int64_t rows_out, int64_t cols_out,
                            int64_t ldo, hipStream_t s);
-hipError_t launch_transpose2(const uint16_t* B, const uint16_t* A, int N, int K, int r, int rp, uint16_t* Bt,
-                             uint16_t* At, hipStream_t s);
+// Bt [r, N] = B^T for B [N, r]; At [K, rp] = A^T zero-padded for A [rA, K] (if At).
+hipError_t launch_transpose2(const uint16_t* B, const uint16_t* A, int N, int K, int r, int rA, int rp,
+                             uint16_t* Bt, uint16_t* At, hipStream_t s);
 hipError_t launch_finalize2(const float* part, int nsplit, int M, int Mp, int r, int rp, float scale,
                             float* P32, uint16_t* Ph, uint16_t* Pl, const float* T, uint16_t* Th,
                             uint16_t* Tl, hipStream_t s);
 hipError_t launch_grad_reduce2(const float* partA, int nsA, int C1, uint16_t* dA, const float* partB, int nsB,
-                               int C2, uint16_t* dB, int r, int rp, float scale, hipStream_t s);
+                               int C2, uint16_t* dB, int rA, int rpA, int rB, int rpB, float scale, hipStream_t s);
 hipError_t launch_gemv(const uint16_t* X, const uint8_t* codes, const uint8_t* c2, const float* c1,
                        const float* absmax, int codebook, int N, int K, int M, const float* tpart, int tsplit,
-                       int rp, const uint16_t* B, int r, float scale, uint16_t* Y, float* T_out, hipStream_t s);
+                       int rp, const uint16_t* B, int r, float scale, uint16_t* Y, float* T_out, hipStream_t s,
+                       int segN = 0, int tld = 0);
 
 // AdamW step (optim.hip): bc1 = 1 / (1 - beta1^t), bc2 = 1 / (1 - beta2^t).
 struct AdamW {

@@ -103,27 +103,38 @@ __global__ __launch_bounds__(256) void proj_kernel(const uint16_t* __restrict__ 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gbl_void_t;
 
-// Same product for Kr % 64 == 0 and rp == 64, streamed: a workgroup owns 64
-// rows of L and a reduction slice; each 64-deep step brings an L tile
-// (64 x 64) and an R tile (64 x 64) into LDS by LDS-DMA, four stages deep,
-// so that ~48 KB per workgroup are in flight. Wave w computes rows 16 w ..
-// 16 w + 15 against all 64 columns (4 MFMA tiles). Rows of R past r and
-// rows of L past M are clamped (their products land in columns / rows
-// nobody reads).
+// Same product for Kr % 64 == 0, streamed: a workgroup owns 64 rows of L, a
+// reduction slice and one 64-column block z of the result (rows 64 z .. of
+// R); each 64-deep step brings an L tile (64 x 64) and an R tile (64 x 64)
+// into LDS by LDS-DMA, four stages deep, so that ~48 KB per workgroup are in
+// flight. Wave w computes rows 16 w .. 16 w + 15 against the block's 64
+// columns (4 MFMA tiles). The rp_total columns come in segments of zper
+// blocks (r_seg valid rows of R each): block z belongs to segment
+// g = z / zper, reads L + g segL and rows 64 (z % zper) .. of R + g segR
+// (row pitches ldL, ldR). One segment (zper >= blocks) is the plain
+// product; several are grouped linears sharing L or slicing L and R by
+// columns. Rows of R past r_seg and rows of L past M are clamped (their
+// products land in columns / rows nobody reads).
 constexpr int PJ_STAGES = 4;
 __device__ __forceinline__ int pj_swz(int R) { return lds_swz(R); }
 
-__global__ __launch_bounds__(256) void proj_stream_kernel(const uint16_t* __restrict__ L,
-                                                           const uint16_t* __restrict__ R, int M,
-                                                           int Kr, int r, int kslice,
+__global__ __launch_bounds__(256) void proj_stream_kernel(const uint16_t* __restrict__ L, int64_t ldL,
+                                                           int64_t segL, const uint16_t* __restrict__ R,
+                                                           int64_t ldR, int64_t segR, int zper, int M,
+                                                           int Kr, int r_seg, int rp_total, int kslice,
                                                            float* __restrict__ part) {
   __shared__ __align__(16) uint16_t sm[PJ_STAGES][2][64 * 64];
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m0 = blockIdx.x * 64;
   const int ks = blockIdx.y;
+  const int z = blockIdx.z;
   const int kbeg = ks * kslice;
   const int nsteps = max(0, min(Kr - kbeg, kslice)) / 64;
+  const int zs = z / zper, zb = z - zs * zper;
+  const int rvalid = min(64, r_seg - 64 * zb);
+  L += zs * segL;
+  R += zs * segR + (int64_t)64 * zb * ldR;
 
   // DMA lanes: wave w fills rows 16 w .. 16 w + 15 of both tiles, two 1 KB
   // instructions each; lane i -> row 16 w + 8 j + (i >> 3), physical chunk
@@ -133,8 +144,8 @@ __global__ __launch_bounds__(256) void proj_stream_kernel(const uint16_t* __rest
   for (int j = 0; j < 2; ++j) {
     const int row = 16 * w + 8 * j + (l >> 3);
     const int c = (l & 7) ^ pj_swz(row);
-    loff[j] = (uint32_t)(min(m0 + row, M - 1) * Kr + 8 * c) * 2u;
-    roff[j] = (uint32_t)(min(row, r - 1) * Kr + 8 * c) * 2u;
+    loff[j] = (uint32_t)(min(m0 + row, M - 1) * ldL + 8 * c) * 2u;
+    roff[j] = (uint32_t)(min(row, rvalid - 1) * ldR + 8 * c) * 2u;
   }
   auto issue = [&](int step) {
     const int slot = step % PJ_STAGES;
@@ -182,13 +193,13 @@ __global__ __launch_bounds__(256) void proj_stream_kernel(const uint16_t* __rest
     }
     __builtin_amdgcn_s_waitcnt(0);  // drain the overrun prefetches before exit
   }
-  float* dst = part + (int64_t)ks * M * 64;
+  float* dst = part + (int64_t)ks * M * rp_total + 64 * z;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int row = m0 + 16 * w + 4 * (l >> 4) + v;
-      if (row < M) dst[(int64_t)row * 64 + 16 * j + (l & 15)] = acc[j][v];
+      if (row < M) dst[(int64_t)row * rp_total + 16 * j + (l & 15)] = acc[j][v];
     }
 }
 
@@ -393,8 +404,8 @@ template <bool TRANS>
 __global__ __launch_bounds__(512) void grad_tr_kernel(const uint16_t* __restrict__ Ph,
                                                        const uint16_t* __restrict__ Pl,
                                                        const uint16_t* __restrict__ Q, int M,
-                                                       int Mp, int C, int rp, int mchunk,
-                                                       float* __restrict__ part) {
+                                                       int Mp, int C, int rp, int mchunk, int segC,
+                                                       int rseg, float* __restrict__ part) {
   extern __shared__ __align__(16) uint16_t gsm[];
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -415,8 +426,12 @@ __global__ __launch_bounds__(512) void grad_tr_kernel(const uint16_t* __restrict
     qrow[q] = 8 * w + 4 * q + (l >> 4);
     qcol[q] = (uint32_t)min(cbase + 8 * ((l & 15) ^ gt_swz_q(qrow[q])), C - 8) * 2u;
   }
+  // segmented (grouped linears): the columns of segment cbase / segC pair
+  // with plane columns (cbase / segC) rseg .. + rseg only; otherwise segC = 0
+  // and the plane block is jc alone. The result has rseg rows j.
+  const int pcol0 = (segC ? (cbase / segC) * rseg : 0) + jc * 64;
   const int prow = 8 * w + (l >> 3);
-  const uint32_t poff = (uint32_t)((mbeg + prow) * rp + jc * 64 + 8 * ((l & 7) ^ gt_swz_p(prow))) * 2u;
+  const uint32_t poff = (uint32_t)((mbeg + prow) * rp + pcol0 + 8 * ((l & 7) ^ gt_swz_p(prow))) * 2u;
   auto issue = [&](int step) {
     uint16_t* st = gsm + (step % GT_STAGES) * GT_STAGE;
     const int ms = min(step, nsteps - 1) * 64;
@@ -479,9 +494,9 @@ __global__ __launch_bounds__(512) void grad_tr_kernel(const uint16_t* __restrict
     if (c >= C) continue;
     if (!TRANS) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) part[((int64_t)s * rp + j0 + v) * C + c] = acc[b][v];
+      for (int v = 0; v < 4; ++v) part[((int64_t)s * rseg + j0 + v) * C + c] = acc[b][v];
     } else {
-      *reinterpret_cast<float4*>(part + ((int64_t)s * C + c) * rp + j0) =
+      *reinterpret_cast<float4*>(part + ((int64_t)s * C + c) * rseg + j0) =
           make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
     }
   }
@@ -523,7 +538,7 @@ __global__ __launch_bounds__(256) void relayout_kernel(const uint16_t* __restric
 // At [K, rp] = A^T with zero columns r .. rp-1 (when At is not null).
 __global__ __launch_bounds__(256) void transpose2_kernel(const uint16_t* __restrict__ B,
                                                           const uint16_t* __restrict__ A, int N,
-                                                          int K, int r, int rp,
+                                                          int K, int r, int rA, int rp,
                                                           uint16_t* __restrict__ Bt,
                                                           uint16_t* __restrict__ At) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
@@ -536,7 +551,7 @@ __global__ __launch_bounds__(256) void transpose2_kernel(const uint16_t* __restr
   const int ia = idx - nb;
   if (!At || ia >= K * rp) return;
   const int k = ia / rp, j = ia - k * rp;
-  At[ia] = j < r ? A[j * K + k] : (uint16_t)0;
+  At[ia] = j < rA ? A[j * K + k] : (uint16_t)0;
 }
 
 // finalize_kernel for the U partials, and in the same launch the hi / lo
@@ -575,34 +590,39 @@ __global__ __launch_bounds__(256) void finalize2_kernel(const float* __restrict_
 __global__ __launch_bounds__(256) void grad_reduce2_kernel(const float* __restrict__ partA, int nsA,
                                                             int C1, uint16_t* __restrict__ dA,
                                                             const float* __restrict__ partB, int nsB,
-                                                            int C2, uint16_t* __restrict__ dB, int r,
-                                                            int rp, float scale) {
+                                                            int C2, uint16_t* __restrict__ dB, int rA,
+                                                            int rpA, int rB, int rpB, float scale) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t na = (int64_t)r * C1;
+  const int64_t na = (int64_t)rA * C1;
   float v = 0.0f;
   if (idx < na) {
     const int64_t j = idx / C1, c = idx % C1;
-    for (int sp = 0; sp < nsA; ++sp) v += partA[((int64_t)sp * rp + j) * C1 + c];
+    for (int sp = 0; sp < nsA; ++sp) v += partA[((int64_t)sp * rpA + j) * C1 + c];
     dA[idx] = __builtin_bit_cast(uint16_t, (__bf16)(scale * v));
     return;
   }
   const int64_t ib = idx - na;
-  if (ib >= (int64_t)C2 * r) return;
-  const int64_t c = ib / r, j = ib % r;
-  for (int sp = 0; sp < nsB; ++sp) v += partB[((int64_t)sp * C2 + c) * rp + j];
+  if (ib >= (int64_t)C2 * rB) return;
+  const int64_t c = ib / rB, j = ib % rB;
+  for (int sp = 0; sp < nsB; ++sp) v += partB[((int64_t)sp * C2 + c) * rpB + j];
   dB[ib] = __builtin_bit_cast(uint16_t, (__bf16)(scale * v));
 }
 
 }  // namespace
 
+hipError_t launch_proj_seg(const uint16_t* L, int64_t ldL, int64_t segL, const uint16_t* R, int64_t ldR,
+                           int64_t segR, int zper, int M, int Kr, int r_seg, int rp_total, int nsplit, float* part,
+                           hipStream_t s) {
+  const int kslice = ((Kr + nsplit - 1) / nsplit + 63) / 64 * 64;
+  dim3 grid((M + 63) / 64, nsplit, rp_total / 64);
+  hipLaunchKernelGGL(proj_stream_kernel, grid, dim3(256), 0, s, L, ldL, segL, R, ldR, segR, zper, M, Kr, r_seg,
+                     rp_total, kslice, part);
+  return hipGetLastError();
+}
+
 hipError_t launch_proj(const uint16_t* L, const uint16_t* R, int M, int Kr, int r, int rp,
                        int nsplit, float* part, hipStream_t s) {
-  if (rp == 64 && Kr % 64 == 0) {
-    const int kslice = ((Kr + nsplit - 1) / nsplit + 63) / 64 * 64;
-    dim3 grid((M + 63) / 64, nsplit);
-    hipLaunchKernelGGL(proj_stream_kernel, grid, dim3(256), 0, s, L, R, M, Kr, r, kslice, part);
-    return hipGetLastError();
-  }
+  if (Kr % 64 == 0) return launch_proj_seg(L, Kr, 0, R, Kr, 0, rp / 64, M, Kr, r, rp, nsplit, part, s);
   const int kslice = ((Kr + nsplit - 1) / nsplit + 31) / 32 * 32;
   if (M <= 16) {
     dim3 grid(1, nsplit);
@@ -639,7 +659,8 @@ hipError_t launch_grad_reduce(const float* part, int nsplit, int r, int rp, int 
 }
 
 hipError_t launch_grad_tr(const uint16_t* Ph, const uint16_t* Pl, const uint16_t* Q, int M, int Mp, int C,
-                          int rp, int nsplit, bool trans, float* part, hipStream_t s) {
+                          int rp, int nsplit, bool trans, float* part, hipStream_t s, int segC, int rseg) {
+  if (!segC) rseg = rp;
   static bool configured = false;  // benign race: every thread sets the same value
   const size_t smem = (size_t)GT_STAGES * GT_STAGE * sizeof(uint16_t);
   if (!configured) {
@@ -652,11 +673,13 @@ hipError_t launch_grad_tr(const uint16_t* Ph, const uint16_t* Pl, const uint16_t
     configured = true;
   }
   const int mchunk = ((Mp + nsplit - 1) / nsplit + 63) / 64 * 64;
-  dim3 grid((C + 127) / 128, nsplit, rp / 64);
+  dim3 grid((C + 127) / 128, nsplit, rseg / 64);
   if (trans)
-    hipLaunchKernelGGL(grad_tr_kernel<true>, grid, dim3(512), smem, s, Ph, Pl, Q, M, Mp, C, rp, mchunk, part);
+    hipLaunchKernelGGL(grad_tr_kernel<true>, grid, dim3(512), smem, s, Ph, Pl, Q, M, Mp, C, rp, mchunk, segC, rseg,
+                       part);
   else
-    hipLaunchKernelGGL(grad_tr_kernel<false>, grid, dim3(512), smem, s, Ph, Pl, Q, M, Mp, C, rp, mchunk, part);
+    hipLaunchKernelGGL(grad_tr_kernel<false>, grid, dim3(512), smem, s, Ph, Pl, Q, M, Mp, C, rp, mchunk, segC, rseg,
+                       part);
   return hipGetLastError();
 }
 
@@ -669,11 +692,11 @@ hipError_t launch_relayout(const uint16_t* in, int64_t rows_in, int64_t cols_in,
   return hipGetLastError();
 }
 
-hipError_t launch_transpose2(const uint16_t* B, const uint16_t* A, int N, int K, int r, int rp, uint16_t* Bt,
-                             uint16_t* At, hipStream_t s) {
+hipError_t launch_transpose2(const uint16_t* B, const uint16_t* A, int N, int K, int r, int rA, int rp,
+                             uint16_t* Bt, uint16_t* At, hipStream_t s) {
   const int64_t total = (int64_t)r * N + (At ? (int64_t)K * rp : 0);
   hipLaunchKernelGGL(transpose2_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, B, A, N, K, r,
-                     rp, Bt, At);
+                     rA, rp, Bt, At);
   return hipGetLastError();
 }
 
@@ -687,10 +710,10 @@ hipError_t launch_finalize2(const float* part, int nsplit, int M, int Mp, int r,
 }
 
 hipError_t launch_grad_reduce2(const float* partA, int nsA, int C1, uint16_t* dA, const float* partB, int nsB,
-                               int C2, uint16_t* dB, int r, int rp, float scale, hipStream_t s) {
-  const int64_t total = (int64_t)r * C1 + (int64_t)C2 * r;
+                               int C2, uint16_t* dB, int rA, int rpA, int rB, int rpB, float scale, hipStream_t s) {
+  const int64_t total = (int64_t)rA * C1 + (int64_t)C2 * rB;
   hipLaunchKernelGGL(grad_reduce2_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, partA, nsA,
-                     C1, dA, partB, nsB, C2, dB, r, rp, scale);
+                     C1, dA, partB, nsB, C2, dB, rA, rpA, rB, rpB, scale);
   return hipGetLastError();
 }
 

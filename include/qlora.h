@@ -220,6 +220,38 @@ int qlora_linear_bwd_4bit(const qlora_4bit_weight* W, const void* X, const void*
                           void* dB, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Grouped linears: several LoRA linears that share one input, as q / k / v
+ * (and gate / up) of a decoder layer do.
+ *
+ * [P2] Introduction (adapters at every network layer) with the layer rule of
+ * qlora_linear_fwd: g segments, segment i with weight W_i [Ns, K] and its own
+ * adapters A_i [r, K], B_i [Ns, r]:
+ *   Y_i = X W_i~^T + scale (X A_i^T) B_i^T             (Y = [Y_1 .. Y_g])
+ *   dX  = sum_i (dY_i W_i~ + scale U_i A_i),  U_i = dY_i B_i
+ *   dA_i = scale U_i^T X,  dB_i = scale dY_i^T T_i,  T_i = X A_i^T
+ * Layouts: W stacks the segments' weights by rows, [g Ns, K], in one stored
+ * 4-bit format (quantising the stacked bf16 weight gives the same codes and
+ * constants as quantising each W_i when Ns K % 16384 == 0). A stacks the
+ * A_i: [g r, K]. B stacks the B_i: [g Ns, r]. X [M, K]; Y and dY [M, g Ns];
+ * T_save / T_saved float32 [M, g r] (T_i in columns i r ..); dX [M, K];
+ * dA [g r, K]; dB [g Ns, r]. The input is read once for all segments (the
+ * projections X A^T and the dA pass), the summed dX comes from one GEMM.
+ * Limits: 1 <= groups <= 16; for groups > 1, Ns % 256 == 0 and r % 64 == 0;
+ * otherwise as for qlora_linear_fwd (with N = g Ns). groups == 1 is
+ * qlora_linear_fwd / _bwd. Errors as there.
+ * ------------------------------------------------------------------------- */
+size_t qlora_linear_grouped_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r,
+                                            int64_t groups);
+int qlora_linear_fwd_grouped(const qlora_4bit_weight* W, int64_t groups, const void* X,
+                             const void* A, const void* B, int64_t M, int64_t r, float scale,
+                             void* Y, float* T_save, void* ws, size_t ws_bytes, void* stream);
+int qlora_linear_bwd_grouped(const qlora_4bit_weight* W, int64_t groups, const void* X,
+                             const void* A, const void* B, const void* dY,
+                             const float* T_saved, int64_t M, int64_t r, float scale,
+                             void* dX, void* dA, void* dB, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* ---------------------------------------------------------------------------
  * Optimizer step of the adapters, with paged optimizer state.
  *
  * [P1] "Paged Optimizers" and [P2] Introduction, contribution (3): optimizer

@@ -212,3 +212,20 @@ def test_adamw_validation(lib):
                 q._AdamWParams(1e-3, 0.9, 0.999, 1e-8, -0.1, 1), q._AdamWParams(1e-3, 0.9, 0.999, 1e-8, 0.0, 0),
                 q._AdamWParams(float("nan"), 0.9, 0.999, 1e-8, 0.0, 1)):
         assert f(FAKE, None, FAKE, FAKE, FAKE, 64, ctypes.byref(bad), None) == UNSUPPORTED
+
+
+def test_grouped_validation(lib):
+    fwd, bwd = lib.qlora_linear_fwd_grouped, lib.qlora_linear_bwd_grouped
+    w = q._Weight4bit(FAKE, FAKE, FAKE, 3 * 256, 128, 0, 1)
+    args = (FAKE, FAKE, FAKE, 16, 64, ctypes.c_float(0.25), FAKE, None, FAKE, 1 << 30, None)
+    assert fwd(ctypes.byref(w), 0, *args) == SHAPE
+    assert fwd(ctypes.byref(w), 17, *args) == SHAPE
+    assert fwd(ctypes.byref(q._Weight4bit(FAKE, FAKE, FAKE, 3 * 200, 128, 0, 1)), 3, *args) == SHAPE  # Ns % 256
+    a33 = (FAKE, FAKE, FAKE, 16, 33, ctypes.c_float(0.25), FAKE, None, FAKE, 1 << 30, None)
+    assert fwd(ctypes.byref(w), 3, *a33) == SHAPE                                                     # r % 64
+    assert fwd(None, 3, *args) == NULL
+    bargs = (FAKE, FAKE, FAKE, FAKE, None, 16, 64, ctypes.c_float(0.25), FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert bwd(ctypes.byref(w), 5, *bargs) == SHAPE                                                   # 768 % 5
+    assert lib.qlora_linear_grouped_workspace_bytes(16, 3 * 256, 128, 64, 3) > 0
+    assert lib.qlora_linear_grouped_workspace_bytes(16, 3 * 200, 128, 64, 3) == 0
+    assert lib.qlora_linear_grouped_workspace_bytes(16, 3 * 256, 128, 32, 3) == 0
