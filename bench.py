@@ -4,11 +4,15 @@
 Step (the timed unit): forward + backward (Y; dX, dA, dB) of the seven LoRA
 linears of a LLaMA-7B-shaped decoder layer (q, k, v, o 4096x4096; gate, up
 11008x4096; down 4096x11008), NF4 + double-quantised weights, LoRA r=64,
-alpha=16, 8192 tokens (16 x 512) per linear; inputs resident in HBM.
+alpha=16, 8192 tokens (16 x 512); inputs resident in HBM. As in a decoder
+layer, q / k / v share one input and gate / up another: they run as grouped
+linears (one pass over the shared input for the projections and dA, one
+GEMM for the summed dX).
 `value` = algorithmic TFLOP/s of the step: sum over linears of
 4 M N K (base forward + input gradient) + 6 M r (K + N) (LoRA), no dW.
 
 Legs timed in the same run (HBM-bound rows of the path):
+  ungrouped the same seven linears run independently, each on its own input
   quantize  NF4 + fp8 DQ of a stack of 65B-class layers (4 x 8192^2 +
             3 x 22016x8192 weights per layer), 2.51587 B moved per weight
   dequant   round trip of the same stack to bf16, 2.51587 B per weight
@@ -62,7 +66,7 @@ def parse():
     ap.add_argument("--config", choices=["7b", "65b"], default="7b",
                     help="layer shapes of the step: LLaMA-7B (default) or 65B-class")
     ap.add_argument("--stack-layers", type=int, default=80, help="65B-class layers in the quantize leg")
-    ap.add_argument("--legs", default="roofline,quantize,gemv,gemm512,formats,adamw",
+    ap.add_argument("--legs", default="ungrouped,roofline,quantize,gemv,gemm512,formats,adamw",
                     help="comma list of extra legs, or 'none'")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -129,10 +133,49 @@ def main():
                    dB=torch.empty(N, r, dtype=torch.bfloat16, device=dev))
         lin.append(dict(name=name, N=N, K=K, W=W, A=A, B=B, X=X, dY=dY, out=out))
         ws_bytes = max(ws_bytes, q.qlora_linear_workspace_bytes(M, N, K, r))
+    # The decoder layer: q / k / v read the same input, and so do gate / up,
+    # so they run as grouped linears (stacked weights and adapters; every
+    # N K here is a whole number of 16384-weight groups, so the stacked
+    # stored weight is the concatenation of the per-linear ones).
+    units = []
+    for name, idx in (("qkv", [0, 1, 2]), ("o", [3]), ("gate_up", [4, 5]), ("down", [6])):
+        Ls = [lin[i] for i in idx]
+        K = Ls[0]["K"]
+        Nt = sum(L["N"] for L in Ls)
+        g = len(Ls)
+        if g == 1:
+            L = Ls[0]
+            units.append(dict(name=name, g=1, N=Nt, K=K, W=L["W"], A=L["A"], B=L["B"], X=L["X"], dY=L["dY"],
+                              out=L["out"]))
+            continue
+        Wst = q.NF4Weight(torch.cat([L["W"].codes for L in Ls]), torch.cat([L["W"].c2 for L in Ls]),
+                          torch.cat([L["W"].c1 for L in Ls]), Nt, K)
+        out = dict(Y=torch.empty(M, Nt, dtype=torch.bfloat16, device=dev),
+                   T=torch.empty(M, g * r, dtype=torch.float32, device=dev),
+                   dX=torch.empty(M, K, dtype=torch.bfloat16, device=dev),
+                   dA=torch.empty(g * r, K, dtype=torch.bfloat16, device=dev),
+                   dB=torch.empty(Nt, r, dtype=torch.bfloat16, device=dev))
+        units.append(dict(name=name, g=g, N=Nt, K=K, W=Wst, A=torch.cat([L["A"] for L in Ls]),
+                          B=torch.cat([L["B"] for L in Ls]), X=Ls[0]["X"],
+                          dY=torch.cat([L["dY"] for L in Ls], dim=1).contiguous(), out=out))
+        ws_bytes = max(ws_bytes, q.qlora_linear_grouped_workspace_bytes(M, Nt, K, r, g))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def step():
+        for U in units:
+            o = U["out"]
+            if U["g"] == 1:
+                q.qlora_linear_fwd(U["W"], U["X"], U["A"], U["B"], s, Y=o["Y"], T=o["T"], workspace=ws)
+                q.qlora_linear_bwd(U["W"], U["X"], U["A"], U["B"], U["dY"], o["T"], s,
+                                   dX=o["dX"], dA=o["dA"], dB=o["dB"], workspace=ws)
+            else:
+                q.qlora_linear_fwd_grouped(U["W"], U["g"], U["X"], U["A"], U["B"], s, Y=o["Y"], T=o["T"],
+                                           workspace=ws)
+                q.qlora_linear_bwd_grouped(U["W"], U["g"], U["X"], U["A"], U["B"], U["dY"], o["T"], s,
+                                           dX=o["dX"], dA=o["dA"], dB=o["dB"], workspace=ws)
+
+    def step_ungrouped():
         for L in lin:
             o = L["out"]
             q.qlora_linear_fwd(L["W"], L["X"], L["A"], L["B"], s, Y=o["Y"], T=o["T"], workspace=ws)
@@ -152,6 +195,16 @@ def main():
 
     legs = {}
     want = set() if args.legs == "none" else set(args.legs.split(","))
+
+    # ---- the same seven linears run independently (no shared inputs) ---------------------
+    if "ungrouped" in want:
+        for _ in range(2):
+            step_ungrouped()
+        reps = max(3, args.steps // 2)
+        tu = timed(step_ungrouped, reps) / reps
+        legs["ungrouped_7_linears"] = {"ms_per_step": round(tu * 1e3, 4),
+                                       "tflops": round(step_flops / tu / 1e12, 2)}
+        log(f"ungrouped 7 linears: {tu * 1e3:.3f} ms, {step_flops / tu / 1e12:.1f} TFLOP/s")
 
     # ---- roofline: dominant kernel, forward orientation over the 7 shapes ----------------
     roofline = None
@@ -398,7 +451,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": ("LLaMA-7B-shaped decoder layer" if args.config == "7b" else "65B-class layer")
                    + ": 7 NF4+DQ linears (q,k,v,o,gate,up,down), LoRA r=64 alpha=16 on each, "
-                   "8192 tokens, forward + backward (dX, dA, dB)",
+                   "q/k/v and gate/up on shared inputs (grouped), 8192 tokens, forward + backward (dX, dA, dB)",
                    "hidden": hidden, "ffn": ffn, "tokens": M, "lora_r": r, "lora_alpha": alpha,
                    "step_tflop": round(step_flops / 1e12, 4), "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4)},
         "roofline": roofline,
