@@ -42,5 +42,6 @@ from .nf4_oracle import (  # noqa: F401
     linear_bwd,
     grouped_linear_fwd,
     grouped_linear_bwd,
+    merge_lora,
 )
 from .adamw import adamw_step  # noqa: F401

@@ -429,3 +429,10 @@ def grouped_linear_bwd(X, W, A, B, dY, s, groups, need_dX=True):
         dA.append(dAi)
         dB.append(dBi)
     return dX, np.concatenate(dA, axis=0), np.concatenate(dB, axis=0)
+
+
+def merge_lora(W, A, B, s):
+    """The merged weight W + s B A in float64 ("Low-Rank Adaptation (LoRA)":
+    x_out = (W_q + B A) x_in), before any rounding."""
+    W, A, B = (np.asarray(t, dtype=np.float64) for t in (W, A, B))
+    return W + float(s) * (B @ A)

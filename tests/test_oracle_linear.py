@@ -71,3 +71,17 @@ def test_single_token_is_dot_products():
         t = [sum(X[0, k] * A[j, k] for k in range(64)) for j in range(2)]
         ref = sum(X[0, k] * W[n, k] for k in range(64)) + s * sum(t[j] * B[n, j] for j in range(2))
         assert abs(Y[0, n] - ref) <= 1e-13
+
+
+def test_merged_weight_reproduces_the_adapted_layer():
+    # the layer rule x_out = (W + s B A) x_in: the merged weight without adapters
+    # gives the same output as the frozen weight with them
+    rng = np.random.default_rng(42)
+    M, N, K, r, s = 9, 33, 70, 6, 0.375
+    X, W = rng.standard_normal((M, K)), rng.standard_normal((N, K))
+    A, B = rng.standard_normal((r, K)), rng.standard_normal((N, r))
+    Wm = oracle.merge_lora(W, A, B, s)
+    Y_adapted, _ = oracle.linear_fwd(X, W, A, B, s)
+    Y_merged, _ = oracle.linear_fwd(X, Wm, np.zeros((r, K)), np.zeros((N, r)), s)
+    np.testing.assert_allclose(Y_merged, Y_adapted, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(oracle.merge_lora(W, A, B, 0.0), W, rtol=0, atol=0)
