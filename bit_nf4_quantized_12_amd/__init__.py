@@ -16,6 +16,7 @@ The function names are those of the C ABI (include/qlora.h):
 * ``qlora_linear_bwd(W, X, A, B, dY, T, scale, ...)``
 * ``qlora_linear_fwd_grouped`` / ``qlora_linear_bwd_grouped``: linears that share
   one input (q / k / v, gate / up), weights and adapters stacked by segment
+* ``qlora_merge_lora(W, A, B, scale)``: the dense bf16 weight W~ + scale B A for serving
 * ``qlora_adamw_step(p32, grad, m, v, step, ...)``: the adapters' optimizer
   step; the state may sit in HBM or in pinned host memory (paged out)
 * ``qlora_levels(codebook)``, ``qlora_quantize_4bit(w, codebook, double_quant)``,
@@ -104,6 +105,7 @@ def load_library(path=LIB_PATH):
             "qlora_levels": ([i32, ctypes.POINTER(ctypes.c_float)], i32),
             "qlora_adamw_step": ([vp, vp, vp, vp, vp, i64, ctypes.POINTER(_AdamWParams), vp], i32),
             "qlora_linear_grouped_workspace_bytes": ([i64, i64, i64, i64, i64], sz),
+            "qlora_merge_lora": ([ctypes.POINTER(_Weight4bit), vp, vp, i64, f32, vp, vp], i32),
             "qlora_linear_fwd_grouped": ([ctypes.POINTER(_Weight4bit), i64, vp, vp, vp, i64, i64, f32, vp, vp, vp, sz, vp], i32),
             "qlora_linear_bwd_grouped": ([ctypes.POINTER(_Weight4bit), i64, vp, vp, vp, vp, vp, i64, i64, f32, vp, vp, vp, vp, sz, vp], i32),
             "qlora_quantize_4bit": ([vp, i64, i32, i32, vp, vp, vp, vp], i32),
@@ -497,3 +499,18 @@ def qlora_linear_bwd_grouped(W, groups, X, A, B, dY, T, scale, need_dX=True, dX=
                                                    _ptr(T), M, r, float(scale), _ptr(dX), _ptr(dA), _ptr(dB),
                                                    _ptr(ws), ws.numel(), _stream(dev)))
     return dX, dA, dB
+
+
+def qlora_merge_lora(W, A, B, scale, out=None):
+    """Dense bf16 weight [N, K] = bf16(W^ + scale B A): the adapters folded into the frozen weight."""
+    _need(A, torch.bfloat16, "A")
+    _need(B, torch.bfloat16, "B")
+    r = A.shape[0]
+    if A.shape != (r, W.cols) or B.shape != (W.rows, r):
+        raise ValueError("shape mismatch: A [r, K], B [N, r], W [N, K]")
+    if out is None:
+        out = torch.empty((W.rows, W.cols), dtype=torch.bfloat16, device=A.device)
+    w = _weight4_struct(W)
+    _check(load_library().qlora_merge_lora(ctypes.byref(w), _ptr(A), _ptr(B), r, float(scale), _ptr(out),
+                                           _stream(A.device)))
+    return out

@@ -641,6 +641,28 @@ int qlora_adamw_step(float* param_f32, void* param_bf16, const void* grad_bf16, 
   }
 }
 
+int qlora_merge_lora(const qlora_4bit_weight* W, const void* A, const void* B, int64_t r, float scale, void* out,
+                     void* stream) {
+  WView v;
+  const int st = view_4bit(W, v);
+  if (st != QLORA_OK) return st;
+  if (!A || !B || !out) return QLORA_ERR_NULL;
+  if (v.N < 1 || v.K < 1 || r < 1 || r > 256 || v.N * v.K >= (int64_t(1) << 40) || v.N >= (int64_t(1) << 31) ||
+      v.K >= (int64_t(1) << 31))
+    return QLORA_ERR_SHAPE;
+  if (!std::isfinite(scale)) return QLORA_ERR_UNSUPPORTED;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(out, 16)) return QLORA_ERR_ALIGN;
+  try {
+    if (tables_status() != 0) return QLORA_ERR_UNSUPPORTED;
+    QLORA_TRY(launch_merge(v.codes, v.c2, v.c1, v.absmax, v.cb, static_cast<const uint16_t*>(A),
+                           static_cast<const uint16_t*>(B), (int)v.N, (int)v.K, (int)r, scale,
+                           static_cast<uint16_t*>(out), (hipStream_t)stream));
+    return QLORA_OK;
+  } catch (...) {
+    return QLORA_ERR_DEVICE;
+  }
+}
+
 size_t qlora_linear_grouped_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r, int64_t groups) {
   if (groups < 1 || groups > 16 || M < 1 || N < 1 || K < 64 || (K % 64) != 0 || r < 1 || r > 256) return 0;
   if (groups > 1 && (N % groups != 0 || (N / groups) % 256 != 0 || r % 64 != 0)) return 0;

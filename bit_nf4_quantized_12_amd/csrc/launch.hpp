@@ -65,6 +65,12 @@ hipError_t launch_gemv(const uint16_t* X, const uint8_t* codes, const uint8_t* c
                        int rp, const uint16_t* B, int r, float scale, uint16_t* Y, float* T_out, hipStream_t s,
                        int segN = 0, int tld = 0);
 
+// Merged weight out [N, K] = bf16(W^ + scale B A) (merge.hip); absmax null:
+// double-quantised constants.
+hipError_t launch_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* absmax, int codebook,
+                        const uint16_t* A, const uint16_t* B, int N, int K, int r, float scale, uint16_t* out,
+                        hipStream_t s);
+
 // AdamW step (optim.hip): bc1 = 1 / (1 - beta1^t), bc2 = 1 / (1 - beta2^t).
 struct AdamW {
   float lr, beta1, beta2, one_minus_beta1, one_minus_beta2, eps, weight_decay, bc1, bc2;

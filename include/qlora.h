@@ -251,6 +251,18 @@ int qlora_linear_bwd_grouped(const qlora_4bit_weight* W, int64_t groups, const v
                              void* dX, void* dA, void* dB, void* ws, size_t ws_bytes,
                              void* stream);
 
+/* Merged weight for deployment: [P1] "Low-Rank Adaptation (LoRA)": the
+ * adapted layer is x_out = (W_q + B A) x_in, so the adapters can be folded
+ * into one dense weight:
+ *   out[n][k] = bf16( fp32( W^[n][k] + fp32(scale * sum_j B[n][j] A[j][k]) ) )
+ * with W^ the exact float32 dequantised weight of W (any stored format), the
+ * sum over j in float32 (ascending j, fused multiply-add), one final
+ * rounding to bf16 (nearest even). A [r, K], B [N, r]: device bf16; out:
+ * device bf16 [N, K]. 1 <= r <= 256. Errors: NULL, SHAPE, ALIGN,
+ * UNSUPPORTED (format or non-finite scale), DEVICE. */
+int qlora_merge_lora(const qlora_4bit_weight* W, const void* A, const void* B, int64_t r,
+                     float scale, void* out, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Optimizer step of the adapters, with paged optimizer state.
  *

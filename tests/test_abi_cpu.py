@@ -229,3 +229,16 @@ def test_grouped_validation(lib):
     assert lib.qlora_linear_grouped_workspace_bytes(16, 3 * 256, 128, 64, 3) > 0
     assert lib.qlora_linear_grouped_workspace_bytes(16, 3 * 200, 128, 64, 3) == 0
     assert lib.qlora_linear_grouped_workspace_bytes(16, 3 * 256, 128, 32, 3) == 0
+
+
+def test_merge_validation(lib):
+    f = lib.qlora_merge_lora
+    w = q._Weight4bit(FAKE, FAKE, FAKE, 64, 64, 0, 1)
+    assert f(None, FAKE, FAKE, 8, ctypes.c_float(1.0), FAKE, None) == NULL
+    assert f(ctypes.byref(w), None, FAKE, 8, ctypes.c_float(1.0), FAKE, None) == NULL
+    assert f(ctypes.byref(w), FAKE, FAKE, 0, ctypes.c_float(1.0), FAKE, None) == SHAPE
+    assert f(ctypes.byref(w), FAKE, FAKE, 257, ctypes.c_float(1.0), FAKE, None) == SHAPE
+    assert f(ctypes.byref(w), FAKE, FAKE, 8, ctypes.c_float(float("inf")), FAKE, None) == UNSUPPORTED
+    assert f(ctypes.byref(w), FAKE + 2, FAKE, 8, ctypes.c_float(1.0), FAKE, None) == ALIGN
+    assert f(ctypes.byref(q._Weight4bit(FAKE, FAKE, FAKE, 64, 64, 9, 1)), FAKE, FAKE, 8, ctypes.c_float(1.0), FAKE,
+             None) == UNSUPPORTED
