@@ -31,6 +31,8 @@ Legs timed in the same run (HBM-bound rows of the path):
             one 22016x8192 weight (each format's own bytes per weight), the
             relative dequantisation error on N(0, 0.02) weights, bits per
             weight, and the forward GEMM at 8192x4096x4096
+  merge     the dense deployment weights bf16(W^ + s B A) of the layer's seven
+            linears (2.52 B moved per weight)
   adamw     the adapters' optimizer step for a 32-layer 7B model (160M LoRA
             parameters, 28 B moved per parameter) with the moments in HBM,
             then paged out to pinned host memory (the kernel works on them
@@ -66,7 +68,7 @@ def parse():
     ap.add_argument("--config", choices=["7b", "65b"], default="7b",
                     help="layer shapes of the step: LLaMA-7B (default) or 65B-class")
     ap.add_argument("--stack-layers", type=int, default=80, help="65B-class layers in the quantize leg")
-    ap.add_argument("--legs", default="ungrouped,roofline,quantize,gemv,gemm512,formats,adamw",
+    ap.add_argument("--legs", default="ungrouped,roofline,quantize,gemv,gemm512,formats,merge,adamw",
                     help="comma list of extra legs, or 'none'")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -379,6 +381,24 @@ def main():
                 del W, Wg
         legs["formats_22016x8192"] = fmt
         del w, wf, Xg, wg, og
+        torch.cuda.empty_cache()
+
+    # ---- merged deployment weights W~ + s B A of the layer's seven linears ----------------
+    if "merge" in want:
+        outs = [torch.empty(L["N"], L["K"], dtype=torch.bfloat16, device=dev) for L in lin]
+
+        def merge_all():
+            for L, o in zip(lin, outs):
+                q.qlora_merge_lora(L["W"], L["A"], L["B"], s, out=o)
+
+        merge_all()
+        tm = timed(merge_all, 5) / 5
+        nw = sum(L["N"] * L["K"] for L in lin)
+        mbytes = nw * (0.5 + 1.0 / 64 + 2.0)  # codes + c2 read, bf16 written (c1, A, B: cache)
+        legs["merge_7b_layer"] = {"weights": nw, "ms": round(tm * 1e3, 3), "GB/s": round(mbytes / tm / 1e9, 1),
+                                  "hbm_frac": round(mbytes / tm / 1e9 / PEAK_HBM_GBS, 4)}
+        log(f"merge: {legs['merge_7b_layer']}")
+        del outs
         torch.cuda.empty_cache()
 
     # ---- the adapters' optimizer step, state in HBM or paged out to pinned host memory -------
