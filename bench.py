@@ -14,8 +14,10 @@ GEMM for the summed dX).
 Legs timed in the same run (HBM-bound rows of the path):
   ungrouped the same seven linears run independently, each on its own input
   quantize  NF4 + fp8 DQ of a stack of 65B-class layers (4 x 8192^2 +
-            3 x 22016x8192 weights per layer), 2.51587 B moved per weight
-  dequant   round trip of the same stack to bf16, 2.51587 B per weight
+            3 x 22016x8192 weights per layer, one batched launch per layer),
+            2.51587 B moved per weight
+  dequant   round trip of the same stack to bf16, 2.51587 B per weight, the
+            outputs rotating over 8 buffers so that nothing stays cached
   gemv      few-token forward (M = 1, 16) of 4096x4096 and 11008x4096 with
             LoRA r=64, rotating over >= 1 GB of distinct weight sets; the
             chain of calls is captured once as a HIP graph and replayed (the
@@ -316,8 +318,10 @@ def main():
         params = sum(w.numel() for w, _ in stack)
 
         def quant_all():
-            for w, o in stack:
-                q.qlora_quantize_nf4_dq(w, out=o)
+            # one launch per layer (its 7 weights)
+            for li in range(0, len(stack), len(per_layer)):
+                layer = stack[li:li + len(per_layer)]
+                q.qlora_quantize_4bit_batch([w for w, _ in layer], "nf4", True, outs=[o for _, o in layer])
 
         quant_all()
         t = timed(quant_all, 3)
@@ -330,11 +334,13 @@ def main():
         # the bf16 input is no longer needed: free it before the round trip
         stack = [(None, o, w.numel()) for w, o in stack]
         torch.cuda.empty_cache()
-        buf = torch.empty(maxn, dtype=torch.bfloat16, device=dev)
+        # outputs rotate over 8 buffers (>= 2.8 GB) so that no output stays in
+        # the 256 MB Infinity Cache between reuses: cold GB/s
+        bufs = [torch.empty(maxn, dtype=torch.bfloat16, device=dev) for _ in range(8)]
 
         def deq_all():
-            for _, (codes, c2, c1), n in stack:
-                q.qlora_dequant(codes, c2, c1, n, torch.bfloat16, out=buf[:n])
+            for i, (_, (codes, c2, c1), n) in enumerate(stack):
+                q.qlora_dequant(codes, c2, c1, n, torch.bfloat16, out=bufs[i % 8][:n])
 
         deq_all()
         t = timed(deq_all, 3)
@@ -343,7 +349,7 @@ def main():
         legs["dequant_bf16_65b_stack"] = {"layers": nl, "ms_per_pass": round(per * 1e3, 3),
                                           "GB/s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
         log(f"dequant bf16: {per * 1e3:.2f} ms, {gbs:.0f} GB/s")
-        del stack, buf
+        del stack, bufs
         torch.cuda.empty_cache()
 
     # ---- the other 4-bit data types and the format without double quantisation ---------------

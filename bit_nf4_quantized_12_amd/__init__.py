@@ -106,6 +106,8 @@ def load_library(path=LIB_PATH):
             "qlora_adamw_step": ([vp, vp, vp, vp, vp, i64, ctypes.POINTER(_AdamWParams), vp], i32),
             "qlora_linear_grouped_workspace_bytes": ([i64, i64, i64, i64, i64], sz),
             "qlora_merge_lora": ([ctypes.POINTER(_Weight4bit), vp, vp, i64, f32, vp, vp], i32),
+            "qlora_quantize_4bit_batch": ([i32, ctypes.POINTER(vp), ctypes.POINTER(i64), i32, i32,
+                                           ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), vp], i32),
             "qlora_linear_fwd_grouped": ([ctypes.POINTER(_Weight4bit), i64, vp, vp, vp, i64, i64, f32, vp, vp, vp, sz, vp], i32),
             "qlora_linear_bwd_grouped": ([ctypes.POINTER(_Weight4bit), i64, vp, vp, vp, vp, vp, i64, i64, f32, vp, vp, vp, vp, sz, vp], i32),
             "qlora_quantize_4bit": ([vp, i64, i32, i32, vp, vp, vp, vp], i32),
@@ -514,3 +516,28 @@ def qlora_merge_lora(W, A, B, scale, out=None):
     _check(load_library().qlora_merge_lora(ctypes.byref(w), _ptr(A), _ptr(B), r, float(scale), _ptr(out),
                                            _stream(A.device)))
     return out
+
+
+def qlora_quantize_4bit_batch(ws, codebook="nf4", double_quant=True, outs=None):
+    """Quantise up to 16 bf16 tensors with one launch -> list of (codes, consts, c1)."""
+    k = len(ws)
+    if not 1 <= k <= 16:
+        raise ValueError("1 to 16 tensors per batch")
+    for i, w in enumerate(ws):
+        _need(w, torch.bfloat16, f"ws[{i}]")
+    if outs is None:
+        outs = []
+        for w in ws:
+            nc, nb, ng = storage_sizes(w.numel())
+            outs.append((torch.empty(nc, dtype=torch.uint8, device=w.device),
+                         torch.empty(nb, dtype=torch.uint8 if double_quant else torch.float32, device=w.device),
+                         torch.empty(ng, dtype=torch.float32, device=w.device) if double_quant else None))
+    arr = ctypes.c_void_p * k
+    wp = arr(*[w.data_ptr() for w in ws])
+    cp = arr(*[o[0].data_ptr() for o in outs])
+    kp = arr(*[o[1].data_ptr() for o in outs])
+    c1p = arr(*[(o[2].data_ptr() if double_quant else 0) for o in outs])
+    n = (ctypes.c_int64 * k)(*[w.numel() for w in ws])
+    _check(load_library().qlora_quantize_4bit_batch(k, wp, n, _codebook_id(codebook), 1 if double_quant else 0,
+                                                    cp, kp, c1p, _stream(ws[0].device)))
+    return outs

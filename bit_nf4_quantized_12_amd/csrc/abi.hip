@@ -560,6 +560,40 @@ int qlora_quantize_4bit(const void* w_bf16, int64_t n, int codebook, int double_
   }
 }
 
+int qlora_quantize_4bit_batch(int count, const void* const* w_bf16, const int64_t* n, int codebook,
+                              int double_quant, uint8_t* const* codes, void* const* consts, float* const* c1,
+                              void* stream) {
+  const int f = check_format(codebook, double_quant);
+  if (f != QLORA_OK) return f;
+  if (count < 1 || count > kQuantBatch) return QLORA_ERR_SHAPE;
+  if (!w_bf16 || !n || !codes || !consts || (double_quant && !c1)) return QLORA_ERR_NULL;
+  QuantBatch b{};
+  b.count = count;
+  b.gstart[0] = 0;
+  for (int t = 0; t < count; ++t) {
+    if (!w_bf16[t] || !codes[t] || !consts[t] || (double_quant && !c1[t])) return QLORA_ERR_NULL;
+    if (n[t] < 1) return QLORA_ERR_SHAPE;
+    if (!aligned(w_bf16[t], 16) || !aligned(codes[t], 16) || !aligned(consts[t], 16) ||
+        (double_quant && !aligned(c1[t], 4)))
+      return QLORA_ERR_ALIGN;
+    b.gstart[t + 1] = b.gstart[t] + cdiv(n[t], kGroup);
+    b.w[t] = static_cast<const uint16_t*>(w_bf16[t]);
+    b.n[t] = n[t];
+    b.codes[t] = codes[t];
+    b.c2[t] = double_quant ? static_cast<uint8_t*>(consts[t]) : nullptr;
+    b.c1[t] = double_quant ? c1[t] : nullptr;
+    b.absmax[t] = double_quant ? nullptr : static_cast<float*>(consts[t]);
+  }
+  if (b.gstart[count] >= (int64_t(1) << 31)) return QLORA_ERR_SHAPE;
+  try {
+    if (tables_status() != 0) return QLORA_ERR_UNSUPPORTED;
+    QLORA_TRY(launch_quantize_batch(b, codebook, (hipStream_t)stream));
+    return QLORA_OK;
+  } catch (...) {
+    return QLORA_ERR_DEVICE;
+  }
+}
+
 int qlora_quantize_nf4_dq(const void* w_bf16, int64_t n, uint8_t* codes, uint8_t* c2_fp8,
                           float* c1, void* stream) {
   if (!w_bf16 || !codes || !c2_fp8 || !c1) return QLORA_ERR_NULL;

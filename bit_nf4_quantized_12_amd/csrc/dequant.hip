@@ -11,7 +11,8 @@
 // into 32 B (fp32) or 16 B (bf16) of output. The 16 levels sit in LDS, where
 // a lookup is conflict free (16 distinct dwords in 16 banks: equal codes
 // broadcast). Bandwidth kernel: 0.5 + 1/64 B read and 4 or 2 B written per
-// weight; four independent words per lane keep loads in flight.
+// weight; four independent words per lane keep loads in flight; the output
+// is written with nontemporal stores (streamed once).
 #include "launch.hpp"
 
 namespace qlora {
@@ -26,11 +27,14 @@ __device__ __forceinline__ void emit8(void* __restrict__ out, int64_t e, uint32_
   if (BF16) {
     uint4 o = make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]),
                          pack_bf16(f[6], f[7]));
-    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + e) = o;
+    const u32x4 ov = {o.x, o.y, o.z, o.w};
+    __builtin_nontemporal_store(ov, reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + e));
   } else {
-    float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + e);
-    p[0] = make_float4(f[0], f[1], f[2], f[3]);
-    p[1] = make_float4(f[4], f[5], f[6], f[7]);
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    f4v* p = reinterpret_cast<f4v*>(reinterpret_cast<float*>(out) + e);
+    const f4v a = {f[0], f[1], f[2], f[3]}, b = {f[4], f[5], f[6], f[7]};
+    __builtin_nontemporal_store(a, p);
+    __builtin_nontemporal_store(b, p + 1);
   }
 }
 

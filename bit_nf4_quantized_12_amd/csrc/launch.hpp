@@ -22,6 +22,21 @@ struct GemmParams {
   Levels lv;
 };
 
+// Several tensors quantised by one launch: workgroups gstart[t] ..
+// gstart[t+1]-1 take the 16384-weight groups of tensor t.
+constexpr int kQuantBatch = 16;
+struct QuantBatch {
+  int count;
+  int64_t gstart[kQuantBatch + 1];
+  const uint16_t* w[kQuantBatch];
+  int64_t n[kQuantBatch];
+  uint8_t* codes[kQuantBatch];
+  uint8_t* c2[kQuantBatch];
+  float* c1[kQuantBatch];
+  float* absmax[kQuantBatch];
+};
+hipError_t launch_quantize_batch(const QuantBatch& b, int codebook, hipStream_t s);
+
 // Double-quantised constants (c2, c1) when absmax is null; otherwise the
 // fp32 block absmax, and c2 / c1 are unused.
 hipError_t launch_quantize(const void* w, int64_t n, int codebook, uint8_t* codes, uint8_t* c2, float* c1,

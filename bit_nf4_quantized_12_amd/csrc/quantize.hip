@@ -9,7 +9,9 @@
 // One workgroup (4 wave64) per group of 256 blocks = 16384 weights = 32 KB
 // of bf16. Loads are 16 B per lane and fully coalesced; the block absmax is
 // a max over the 8 lanes that hold a block (DPP, no LDS); the group max is a
-// wave reduction plus 4 LDS slots. HBM traffic is the algorithmic minimum:
+// wave reduction plus 4 LDS slots. The weights are read and the codes
+// written with nontemporal accesses (streamed once; measured +4-5 % on a
+// cold 3.4 GB pass). HBM traffic is the algorithmic minimum:
 // 2 B read and 0.5 + 1/64 + 4/16384 B written per weight (0.5 + 4/64 B
 // without double quantisation, when the fp32 block absmax is stored as is).
 // The data type only changes the search table passed in.
@@ -65,19 +67,27 @@ __device__ __forceinline__ uint32_t e4m3_code(float rho) {
   return (uint32_t)__builtin_rintf(rho * 512.0f);  // subnormal: m * 2^-9, m in 0..8
 }
 
-__global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ w, int64_t n,
-                                                        uint8_t* __restrict__ codes,
-                                                        uint8_t* __restrict__ c2,
-                                                        float* __restrict__ c1,
-                                                        float* __restrict__ absmax_out, QuantTable qt) {
+__global__ __launch_bounds__(256) void quantize_kernel(QuantBatch bt, QuantTable qt) {
   __shared__ float2 s_tab[32];
   __shared__ float s_wmax[4];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   if (tid < 32) s_tab[tid] = make_float2(qt.thr[tid], __int_as_float(qt.base[tid]));
+
+  // this workgroup's tensor (uniform scan over at most kQuantBatch entries)
+  // and its group within that tensor
+  int ti = 0;
+  while (ti + 1 < bt.count && (int64_t)blockIdx.x >= bt.gstart[ti + 1]) ++ti;
+  const uint16_t* __restrict__ w = bt.w[ti];
+  const int64_t n = bt.n[ti];
+  uint8_t* __restrict__ codes = bt.codes[ti];
+  uint8_t* __restrict__ c2 = bt.c2[ti];
+  float* __restrict__ c1 = bt.c1[ti];
+  float* __restrict__ absmax_out = bt.absmax[ti];
+  const int64_t grp = (int64_t)blockIdx.x - bt.gstart[ti];
   __syncthreads();
 
-  const int64_t gbase = (int64_t)blockIdx.x * kGroup;
+  const int64_t gbase = grp * kGroup;
   const int64_t nb = (n + kBlock - 1) / kBlock;
   const bool full = gbase + kGroup <= n;
 
@@ -86,7 +96,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int64_t e = gbase + wave * 4096 + j * 512 + lane * 8;
-      v[j] = *reinterpret_cast<const uint4*>(w + e);
+      const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w + e));
+      v[j] = make_uint4(t[0], t[1], t[2], t[3]);
     }
   } else {
 #pragma unroll
@@ -128,7 +139,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
       }
     }
     if (full || e + 8 <= n) {
-      *reinterpret_cast<uint32_t*>(codes + (e >> 1)) = word;
+      __builtin_nontemporal_store(word, reinterpret_cast<uint32_t*>(codes + (e >> 1)));
     } else if (e < n) {
       // short tail: elements past n get code 0, bytes past ceil(n/2) are not written
       const int valid = (int)(n - e);
@@ -154,7 +165,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   if (lane == 0) s_wmax[wave] = gmax;
   __syncthreads();
   const float g = fmaxf(fmaxf(s_wmax[0], s_wmax[1]), fmaxf(s_wmax[2], s_wmax[3]));
-  if (tid == 0) c1[blockIdx.x] = g;
+  if (tid == 0) c1[grp] = g;
   if ((lane & 7) == 0) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -170,12 +181,25 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
 
 }  // namespace
 
+hipError_t launch_quantize_batch(const QuantBatch& b, int codebook, hipStream_t s) {
+  const int64_t groups = b.gstart[b.count];
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)groups), dim3(256), 0, s, b, host_quant_table(codebook));
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize(const void* w, int64_t n, int codebook, uint8_t* codes, uint8_t* c2, float* c1,
                            float* absmax, hipStream_t s) {
-  const int64_t groups = (n + kGroup - 1) / kGroup;
-  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)groups), dim3(256), 0, s,
-                     reinterpret_cast<const uint16_t*>(w), n, codes, c2, c1, absmax, host_quant_table(codebook));
-  return hipGetLastError();
+  QuantBatch b{};
+  b.count = 1;
+  b.gstart[0] = 0;
+  b.gstart[1] = (n + kGroup - 1) / kGroup;
+  b.w[0] = reinterpret_cast<const uint16_t*>(w);
+  b.n[0] = n;
+  b.codes[0] = codes;
+  b.c2[0] = c2;
+  b.c1[0] = c1;
+  b.absmax[0] = absmax;
+  return launch_quantize_batch(b, codebook, s);
 }
 
 }  // namespace qlora

@@ -199,6 +199,17 @@ int qlora_levels(int codebook, float out[16]);
 int qlora_quantize_4bit(const void* w_bf16, int64_t n, int codebook, int double_quant,
                         uint8_t* codes, void* consts, float* c1, void* stream);
 
+/* Quantise count (1 .. 16) tensors with one launch, as qlora_quantize_4bit
+ * would quantise each (bulk quantisation of a model: one launch per layer
+ * instead of one per tensor). w_bf16, n, codes, consts, c1: host arrays of
+ * count entries holding each tensor's device pointers and size (c1 ignored,
+ * and may be NULL, without double quantisation). Errors: NULL, SHAPE (count
+ * out of range, an n < 1, more than 2^31 - 1 groups of 16384 in all),
+ * ALIGN, UNSUPPORTED, DEVICE; nothing is launched on any error. */
+int qlora_quantize_4bit_batch(int count, const void* const* w_bf16, const int64_t* n,
+                              int codebook, int double_quant, uint8_t* const* codes,
+                              void* const* consts, float* const* c1, void* stream);
+
 /* Dequantise n weights of a stored 4-bit format to float32 (W^) or bf16
  * (W~): [P2] "Method". Inputs as written by qlora_quantize_4bit with the
  * same codebook and double_quant. Errors: NULL, SHAPE, ALIGN, UNSUPPORTED,

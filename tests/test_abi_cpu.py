@@ -242,3 +242,18 @@ def test_merge_validation(lib):
     assert f(ctypes.byref(w), FAKE + 2, FAKE, 8, ctypes.c_float(1.0), FAKE, None) == ALIGN
     assert f(ctypes.byref(q._Weight4bit(FAKE, FAKE, FAKE, 64, 64, 9, 1)), FAKE, FAKE, 8, ctypes.c_float(1.0), FAKE,
              None) == UNSUPPORTED
+
+
+def test_quantize_batch_validation(lib):
+    f = lib.qlora_quantize_4bit_batch
+    arr = ctypes.c_void_p * 2
+    ok = arr(FAKE, FAKE)
+    n = (ctypes.c_int64 * 2)(64, 64)
+    assert f(0, ok, n, 0, 1, ok, ok, ok, None) == SHAPE
+    assert f(17, ok, n, 0, 1, ok, ok, ok, None) == SHAPE
+    assert f(2, None, n, 0, 1, ok, ok, ok, None) == NULL
+    assert f(2, ok, n, 0, 1, ok, ok, None, None) == NULL           # c1 needed with double quantisation
+    assert f(2, ok, n, 3, 1, ok, ok, ok, None) == UNSUPPORTED
+    assert f(2, ok, (ctypes.c_int64 * 2)(64, 0), 0, 1, ok, ok, ok, None) == SHAPE
+    assert f(2, arr(FAKE, FAKE + 2), n, 0, 1, ok, ok, ok, None) == ALIGN
+    assert f(2, ok, n, 0, 1, arr(FAKE, None), ok, ok, None) == NULL

@@ -156,3 +156,23 @@ def test_linear_fwd_bwd(cb, dq, M, N, K, r):
 def test_llama7b_projection_sampled_rows(cb, dq):
     rows = np.random.default_rng(5).choice(2048, 96, replace=False)
     _run_linear(2048, 4096, 4096, 64, 16.0, cb, dq, rows=rows)
+
+
+@pytest.mark.parametrize("cb,dq", [("nf4", True), ("int4", False), ("fp4", True)])
+def test_batch_quantise_equals_per_tensor_and_oracle(cb, dq):
+    sizes = [1, 65, 16384, 3 * 16384 + 77, 100003, 64 * 16384]
+    ts = [synth.normal((n,), 0.02, 0, (95, n, 0)) for n in sizes]
+    ws = [t.reshape(-1).to(DEV) for t, _ in ts]
+    batch = q.qlora_quantize_4bit_batch(ws, cb, dq)
+    torch.cuda.synchronize()
+    for (t, w32), w, got in zip(ts, ws, batch):
+        one = q.qlora_quantize_4bit(w, cb, dq)
+        for x, y in zip(got, one):
+            assert (x is None and y is None) or torch.equal(x, y)
+        pk, oc, oc1, _ = _oracle_quant(w32, cb, dq)
+        np.testing.assert_array_equal(got[0].cpu().numpy(), pk)
+        if dq:
+            np.testing.assert_array_equal(got[1].cpu().numpy(), oc)
+            np.testing.assert_array_equal(got[2].cpu().numpy().view(np.uint32), oc1.view(np.uint32))
+        else:
+            np.testing.assert_array_equal(got[1].cpu().numpy().view(np.uint32), oc.view(np.uint32))
