@@ -37,8 +37,10 @@ struct Layout {
   size_t partT = 0, T32 = 0, Ts = 0, Bpad = 0;                       // forward
   size_t Bt = 0, At = 0, partU = 0, U32 = 0, PtH = 0, PtL = 0, TtH = 0, TtL = 0;  // backward
   size_t gpartA = 0, gpartB = 0;
+  size_t partY = 0, partX = 0;  // split-reduction partials of the Y / dX GEMMs
   size_t fwd_total = 0, bwd_total = 0;
   int tsplit = 1, usplit = 1, sA = 1, sB = 1;
+  int ksY = 1, kcY = 0, ksX = 1, kcX = 0;
 };
 
 Layout plan(int64_t M, int64_t N, int64_t K, int64_t r) {
@@ -51,6 +53,8 @@ Layout plan(int64_t M, int64_t N, int64_t K, int64_t r) {
   L.T32 = o;   o = al256(o + (size_t)M * r * 4);
   L.Ts = o;    o = al256(o + (size_t)M * rp * 2);
   L.Bpad = o;  o = al256(o + (rp != r ? (size_t)N * rp * 2 : 0));
+  if (M > kGemvMaxM) L.ksY = gemm_ksplit(M, N, K, &L.kcY);
+  L.partY = o; o = al256(o + (L.ksY > 1 ? (size_t)L.ksY * M * N * 4 : 0));
   L.fwd_total = o;
   // backward (T recompute reuses the forward region [partT, Ts))
   L.usplit = proj_splits(M, N);
@@ -68,6 +72,8 @@ Layout plan(int64_t M, int64_t N, int64_t K, int64_t r) {
   L.TtL = o;   o = al256(o + (size_t)rp * Mp * 2);
   L.gpartA = o; o = al256(o + (size_t)L.sA * rp * K * 4);
   L.gpartB = o; o = al256(o + (size_t)L.sB * rp * N * 4);
+  L.ksX = gemm_ksplit(M, K, N, &L.kcX);
+  L.partX = o; o = al256(o + (L.ksX > 1 ? (size_t)L.ksX * M * K * 4 : 0));
   L.bwd_total = o;
   return L;
 }
@@ -251,6 +257,9 @@ int fwd_impl(const WView& W, const void* X, const void* A, const void* B, int64_
     p.Nout = (int)N;
     p.Kred = (int)K;
     p.lv = host_levels(W.cb);
+    p.ksplit = L.ksY;
+    p.kchunk = L.kcY;
+    p.part = reinterpret_cast<float*>(base + L.partY);
     QLORA_TRY(launch_gemm(p, false, s));
     return QLORA_OK;
   } catch (...) {
@@ -320,7 +329,7 @@ int bwd_impl(const WView& W, const void* X, const void* A, const void* B, const 
       p.codes = W.codes;
       p.c2 = W.c2;
       p.c1 = W.c1;
-    p.absmax = W.absmax;
+      p.absmax = W.absmax;
       p.wN = N;
       p.wK = K;
       p.lora_l = PtH;
@@ -333,6 +342,9 @@ int bwd_impl(const WView& W, const void* X, const void* A, const void* B, const 
       p.Nout = (int)K;
       p.Kred = (int)N;
       p.lv = host_levels(W.cb);
+      p.ksplit = L.ksX;
+      p.kchunk = L.kcX;
+      p.part = reinterpret_cast<float*>(base + L.partX);
       QLORA_TRY(launch_gemm(p, true, s));
     }
     // dA = (s U)^T X  [r, K] (K % 64 == 0); dB = s dY^T T  [N, r], computed as
@@ -415,6 +427,9 @@ int fwd_grouped_impl(const WView& W, int64_t g, const void* X, const void* A, co
     p.Nout = (int)N;
     p.Kred = (int)K;
     p.lv = host_levels(W.cb);
+    p.ksplit = L.ksY;
+    p.kchunk = L.kcY;
+    p.part = reinterpret_cast<float*>(base + L.partY);
     QLORA_TRY(launch_gemm(p, false, s));
     return QLORA_OK;
   } catch (...) {
@@ -494,6 +509,9 @@ int bwd_grouped_impl(const WView& W, int64_t g, const void* X, const void* A, co
       p.Nout = (int)K;
       p.Kred = (int)N;
       p.lv = host_levels(W.cb);
+      p.ksplit = L.ksX;
+      p.kchunk = L.kcX;
+      p.part = reinterpret_cast<float*>(base + L.partX);
       QLORA_TRY(launch_gemm(p, true, s));
     }
     // dA_i = (s U_i)^T X for all segments in one pass over X; dB_i from dY_i

@@ -196,15 +196,23 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
 
   // XCD-aware tile order: workgroup g runs on XCD g % 8; XCD x owns the
   // contiguous tile range [x * per, (x + 1) * per) in row-major tile order.
+  // Split reduction (few tiles): work item u = tile t, split ks of the
+  // reduction steps [ks kchunk, ks kchunk + kchunk); splits write float32
+  // partial tiles that a second kernel sums.
   const int gn = (p.Nout + BN - 1) / BN;
   const int gm = (p.M + BM - 1) / BM;
   const int tiles = gn * gm;
-  const int per = (tiles + 7) / 8;
-  const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (t >= tiles) return;
+  const int total = tiles * p.ksplit;
+  const int per = (total + 7) / 8;
+  const int u = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (u >= total) return;
+  const int t = u / p.ksplit, ksp = u - t * p.ksplit;
   const int m0 = (t / gn) * BM;
   const int n0 = (t % gn) * BN;
   const int nk = (p.Kred + BK - 1) / BK;
+  const int kchunk = p.ksplit > 1 ? p.kchunk : nk;
+  const int kbeg = ksp * kchunk;
+  const int kend = min(nk, kbeg + kchunk);
 
   // ---- activation tile of step kt -> stage st --------------------------------------
   // VEC (Kred % 64 == 0): LDS-DMA, 16 B per lane; instruction j of wave w
@@ -278,11 +286,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // prologue: stage 0 complete, codes of step 1 in flight
-  load_x(0, 0);
-  WPart<QW> wnext = load_w(0);
+  // prologue: stage 0 complete, codes of the next step in flight
+  load_x(kbeg, 0);
+  WPart<QW> wnext = load_w(kbeg);
   store_wpart<TW, QW>(wnext, p.lv, sB, tid);
-  wnext = load_w(1);
+  wnext = load_w(kbeg + 1);
   __builtin_amdgcn_s_waitcnt(0);  // stage 0 LDS-DMA landed (vmcnt = lgkmcnt = 0)
   __syncthreads();
 
@@ -293,8 +301,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
   const int ck0 = 8 * ((0 + (l >> 4)) ^ swz(l & 15));
   const int ck1 = 8 * ((4 + (l >> 4)) ^ swz(l & 15));
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
+  for (int kt = kbeg; kt < kend; ++kt) {
+    const int st = (kt - kbeg) & 1;
     load_x(kt + 1, st ^ 1);
     const WPart<QW> wcur = wnext;
     wnext = load_w(kt + 2);
@@ -321,7 +329,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
     __syncthreads();
   }
 
-  if (LORA) {
+  if (LORA && ksp == 0) {
     // acc += lora_l[rows, :] lora_r[cols, :]^T, 64 rank columns per step
     // (rp is a multiple of 64, zero padded), staged through LDS stage 0 by
     // LDS-DMA like the main loop; the loop ended on a barrier.
@@ -365,6 +373,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
   }
 
   // D layout of a 16 x 16 tile: lane holds rows 4 (l >> 4) + v, column l & 15
+  float* __restrict__ part = p.ksplit > 1 ? p.part + (int64_t)ksp * p.M * p.Nout : nullptr;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -375,11 +384,37 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
       for (int v = 0; v < 4; ++v) {
         const int row = m0 + wm * 128 + 16 * i + 4 * (l >> 4) + v;
         if (row < p.M) {
-          const __bf16 h = (__bf16)acc[i][j][v];
-          p.out[(int64_t)row * p.Nout + col] = __builtin_bit_cast(uint16_t, h);
+          if (part) {
+            part[(int64_t)row * p.Nout + col] = acc[i][j][v];
+          } else {
+            const __bf16 h = (__bf16)acc[i][j][v];
+            p.out[(int64_t)row * p.Nout + col] = __builtin_bit_cast(uint16_t, h);
+          }
         }
       }
     }
+}
+
+// out = bf16(sum over the splits of the float32 partial tiles), fixed order.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int ksplit, int64_t mn,
+                                                             uint16_t* __restrict__ out) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= mn) return;
+  // 16-byte partial loads need mn % 4 == 0; the 8-byte store an aligned out
+  if (i + 4 <= mn && (mn & 3) == 0 && ((uintptr_t)out & 7) == 0) {
+    float4 acc = *reinterpret_cast<const float4*>(part + i);
+    for (int s = 1; s < ksplit; ++s) {
+      const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)s * mn + i);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    *reinterpret_cast<uint2*>(out + i) = make_uint2(pack_bf16(acc.x, acc.y), pack_bf16(acc.z, acc.w));
+    return;
+  }
+  for (int64_t e = i; e < min(mn, i + 4); ++e) {
+    float a = part[e];
+    for (int s = 1; s < ksplit; ++s) a += part[(int64_t)s * mn + e];
+    out[e] = __builtin_bit_cast(uint16_t, (__bf16)a);
+  }
 }
 
 template <int BM, int BN, bool TW, bool LORA, bool VEC, bool ABS>
@@ -393,8 +428,13 @@ hipError_t launch_variant(const GemmParams& p, hipStream_t s) {
     configured = true;
   }
   const int tiles = ((p.Nout + BN - 1) / BN) * ((p.M + BM - 1) / BM);
-  const int grid = 8 * ((tiles + 7) / 8);
+  const int grid = 8 * ((tiles * p.ksplit + 7) / 8);
   hipLaunchKernelGGL((gemm_kernel<BM, BN, TW, LORA, VEC, ABS>), dim3(grid), dim3(NT), smem_bytes, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.ksplit <= 1) return e;
+  const int64_t mn = (int64_t)p.M * p.Nout;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((mn / 4 + 255) / 256 + 1)), dim3(256), 0, s, p.part,
+                     p.ksplit, mn, p.out);
   return hipGetLastError();
 }
 

@@ -20,7 +20,30 @@ struct GemmParams {
   uint16_t* out;           // [M, Nout] bf16
   int M, Nout, Kred;
   Levels lv;
+  // split reduction: ksplit > 1 splits of kchunk 64-deep steps write float32
+  // partial tiles to part [ksplit][M][Nout], summed into out afterwards
+  int ksplit = 1, kchunk = 0;
+  float* part = nullptr;
 };
+
+// Splits of the reduction for a GEMM with few output tiles: ~256 workgroups,
+// at most 8 splits of at least 4 steps each; 1 from 192 tiles on. Returns
+// the split count (every split non-empty) and the steps per split.
+inline int gemm_ksplit(int64_t M, int64_t Nout, int64_t Kred, int* kchunk) {
+  const int64_t BMs = M >= 1024 ? 512 : 256, BNs = M >= 1024 ? 128 : 256;
+  const int64_t tiles = ((M + BMs - 1) / BMs) * ((Nout + BNs - 1) / BNs);
+  const int64_t nk = (Kred + 63) / 64;
+  int64_t ks = 1;
+  if (tiles < 192) {
+    ks = (256 + tiles - 1) / tiles;
+    if (ks > 8) ks = 8;
+    if (ks > nk / 4) ks = nk / 4;
+    if (ks < 1) ks = 1;
+  }
+  const int64_t ch = (nk + ks - 1) / ks;
+  *kchunk = (int)ch;
+  return (int)((nk + ch - 1) / ch);
+}
 
 // Several tensors quantised by one launch: workgroups gstart[t] ..
 // gstart[t+1]-1 take the 16384-weight groups of tensor t.

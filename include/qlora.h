@@ -114,7 +114,10 @@ int qlora_nf4_matmul(const qlora_nf4_weight* W, const void* act, int64_t M, int 
                      void* out, void* stream);
 
 /* Workspace bytes needed by qlora_linear_fwd and qlora_linear_bwd for these
- * sizes (the larger of the two; 0 on invalid sizes). */
+ * sizes (the larger of the two; 0 on invalid sizes). When a product has few
+ * output tiles (M of a few hundred tokens), its reduction is split and the
+ * float32 partial products live in the workspace; they are summed in a fixed
+ * order, so results stay bit-identical from run to run. */
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
 
 /* LoRA linear forward on the frozen quantised weight:

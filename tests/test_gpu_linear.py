@@ -116,6 +116,32 @@ def test_backward_is_deterministic():
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("M,N,K,r", [
+    # few output tiles: the GEMM reduction is split (8 splits of 8 steps, the
+    # last of 7; the dX product 4 splits over a ragged 1000-long reduction)
+    (300, 1000, 4032, 64),
+    # 512 x 128 tiles, 15 of them: 8 splits of 4 steps
+    (1100, 520, 2048, 32),
+    (512, 4096, 4096, 64),
+])
+def test_split_reduction_shapes(M, N, K, r):
+    rows = None if M <= 300 else np.random.default_rng(M + N).choice(M, 128, replace=False)
+    run_case(M, N, K, r, 16.0, cfg=105, rows=rows)
+
+
+def test_split_reduction_is_deterministic():
+    case = synth.linear_case(512, 1000, 4096, 64, cfg=106)
+    Wt, Xt, At, Bt, dYt = (case[k][0].to(DEV) for k in ("W", "X", "A", "B", "dY"))
+    W = q.quantize_weight(Wt)
+    outs = []
+    for _ in range(2):
+        Y, T = q.qlora_linear_fwd(W, Xt, At, Bt, 0.25)
+        outs.append((Y,) + tuple(q.qlora_linear_bwd(W, Xt, At, Bt, dYt, T, 0.25)))
+    torch.cuda.synchronize()
+    for x, y in zip(*outs):
+        assert torch.equal(x, y)
+
+
 @pytest.mark.parametrize("M", [1, 16, 512])
 @pytest.mark.parametrize("N", [4096, 11008])
 def test_llama7b_projections_forward(M, N):
