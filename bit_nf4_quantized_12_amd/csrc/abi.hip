@@ -47,7 +47,8 @@ Layout plan(int64_t M, int64_t N, int64_t K, int64_t r) {
   Layout L;
   const int64_t rp = cdiv(r, 64) * 64;
   // forward
-  L.tsplit = proj_splits(M, K);
+  int kslice = 0;
+  L.tsplit = M <= kGemvMaxM ? proj_small_splits((int)K, &kslice) : proj_splits(M, K);
   size_t o = 0;
   L.partT = o; o = al256(o + (size_t)L.tsplit * M * rp * 4);
   L.T32 = o;   o = al256(o + (size_t)M * r * 4);
@@ -167,6 +168,16 @@ bool device_address(const void* p, void** out) {
     if ((expr) != hipSuccess) return QLORA_ERR_DEVICE; \
   } while (0)
 
+// T = X A^T as split partials [tsplit][M][rp] (tsplit from plan()); A [r, K]
+// (the stacked A of grouped linears: r = g r_seg). Few tokens
+// take the all-loads-in-flight kernel; it is also the one the backward's
+// recompute uses, so a saved and a recomputed T are bit-identical.
+hipError_t project_T(const uint16_t* X, const uint16_t* A, int64_t M, int64_t K, int64_t r, int rp, int tsplit,
+                     float* partT, hipStream_t s) {
+  if (M <= kGemvMaxM) return launch_proj_small(X, A, (int)M, (int)K, (int)r, rp, partT, s);
+  return launch_proj(X, A, (int)M, (int)K, (int)r, rp, tsplit, partT, s);
+}
+
 int matmul_impl(const WView& W, const void* act, int64_t M, int transposed, void* out, void* stream) {
   if (!act || !out) return QLORA_ERR_NULL;
   const int64_t N = W.N, K = W.K;
@@ -223,7 +234,7 @@ int fwd_impl(const WView& W, const void* X, const void* A, const void* B, int64_
     const uint16_t* Bh = static_cast<const uint16_t*>(B);
 
     // T = X A^T: split-K partials [tsplit][M][rp]
-    QLORA_TRY(launch_proj(Xh, Ah, (int)M, (int)K, (int)r, rp, L.tsplit, partT, s));
+    QLORA_TRY(project_T(Xh, Ah, M, K, r, rp, L.tsplit, partT, s));
     if (M <= kGemvMaxM) {
       // few tokens: one weight-streaming kernel, which also sums the T
       // partials, adds the LoRA term and writes T_save
@@ -309,7 +320,7 @@ int bwd_impl(const WView& W, const void* X, const void* A, const void* B, const 
       float* partT = reinterpret_cast<float*>(base + L.partT);
       float* T32 = reinterpret_cast<float*>(base + L.T32);
       uint16_t* Ts = reinterpret_cast<uint16_t*>(base + L.Ts);
-      QLORA_TRY(launch_proj(Xh, Ah, (int)M, (int)K, (int)r, rp, L.tsplit, partT, s));
+      QLORA_TRY(project_T(Xh, Ah, M, K, r, rp, L.tsplit, partT, s));
       QLORA_TRY(launch_finalize(partT, L.tsplit, (int)M, (int)M, (int)r, rp, 1.0f, T32, Ts, nullptr, s));
       T = T32;
     }
@@ -402,7 +413,7 @@ int fwd_grouped_impl(const WView& W, int64_t g, const void* X, const void* A, co
     const uint16_t* Ah = static_cast<const uint16_t*>(A);
     const uint16_t* Bh = static_cast<const uint16_t*>(B);
     // T = X [A_1; ..; A_g]^T: one pass over X for all segments
-    QLORA_TRY(launch_proj_seg(Xh, K, 0, Ah, K, 0, (int)(R / 64), (int)M, (int)K, (int)R, (int)R, L.tsplit, partT, s));
+    QLORA_TRY(project_T(Xh, Ah, M, K, R, (int)R, L.tsplit, partT, s));
     if (M <= kGemvMaxM) {
       QLORA_TRY(launch_gemv(Xh, W.codes, W.c2, W.c1, W.absmax, W.cb, (int)N, (int)K, (int)M, partT, L.tsplit,
                             (int)R, Bh, (int)r, scale, static_cast<uint16_t*>(Y), T_save, s, (int)Ns, (int)R));
@@ -477,8 +488,7 @@ int bwd_grouped_impl(const WView& W, int64_t g, const void* X, const void* A, co
       float* partT = reinterpret_cast<float*>(base + L.partT);
       float* T32 = reinterpret_cast<float*>(base + L.T32);
       uint16_t* Ts = reinterpret_cast<uint16_t*>(base + L.Ts);
-      QLORA_TRY(launch_proj_seg(Xh, K, 0, Ah, K, 0, (int)(R / 64), (int)M, (int)K, (int)R, (int)R, L.tsplit, partT,
-                                s));
+      QLORA_TRY(project_T(Xh, Ah, M, K, R, (int)R, L.tsplit, partT, s));
       QLORA_TRY(launch_finalize(partT, L.tsplit, (int)M, (int)M, (int)R, (int)R, 1.0f, T32, Ts, nullptr, s));
       T = T32;
     }

@@ -98,6 +98,12 @@ hipError_t launch_finalize2(const float* part, int nsplit, int M, int Mp, int r,
                             uint16_t* Tl, hipStream_t s);
 hipError_t launch_grad_reduce2(const float* partA, int nsA, int C1, uint16_t* dA, const float* partB, int nsB,
                                int C2, uint16_t* dB, int rA, int rpA, int rB, int rpB, float scale, hipStream_t s);
+// Few tokens (M <= 16): split count of T = X R^T for launch_proj_small
+// (at most 8 slices of kslice columns, a multiple of 128) and its launch:
+// part [splits][M][rp] float32, columns j < rows written.
+int proj_small_splits(int K, int* kslice);
+hipError_t launch_proj_small(const uint16_t* X, const uint16_t* R, int M, int K, int rows, int rp, float* part,
+                             hipStream_t s);
 hipError_t launch_gemv(const uint16_t* X, const uint8_t* codes, const uint8_t* c2, const float* c1,
                        const float* absmax, int codebook, int N, int K, int M, const float* tpart, int tsplit,
                        int rp, const uint16_t* B, int r, float scale, uint16_t* Y, float* T_out, hipStream_t s,

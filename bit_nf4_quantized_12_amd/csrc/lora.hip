@@ -204,28 +204,53 @@ __global__ __launch_bounds__(256) void proj_stream_kernel(const uint16_t* __rest
 }
 
 // Sum the reduction slices: P32 [M, r] float32 (may be null) and
-// Ps [M, rp] = bf16(scale * P), zero in columns r .. rp-1.
+// Ps [M, rp] = bf16(scale * P), zero in columns r .. rp-1. A thread takes 4
+// adjacent columns (rp % 4 == 0); slices are added in order, from 0.
+__device__ __forceinline__ float4 sum_slices(const float* __restrict__ part, int nsplit, int64_t slice, int64_t i4) {
+  float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  const float4* p4 = reinterpret_cast<const float4*>(part + i4);
+  const int64_t st = slice / 4;
+#pragma unroll 8
+  for (int s = 0; s < nsplit; ++s) {
+    const float4 x = p4[s * st];
+    v.x += x.x; v.y += x.y; v.z += x.z; v.w += x.w;
+  }
+  return v;
+}
+
+__device__ __forceinline__ void store_hi_lo(uint16_t* __restrict__ Ph, uint16_t* __restrict__ Pl, int64_t i4,
+                                            const float (&sv)[4]) {
+  uint16_t h[4], lo[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const __bf16 b = (__bf16)sv[e];
+    h[e] = __builtin_bit_cast(uint16_t, b);
+    lo[e] = __builtin_bit_cast(uint16_t, (__bf16)(sv[e] - (float)b));
+  }
+  *reinterpret_cast<uint2*>(Ph + i4) = make_uint2(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16);
+  if (Pl) *reinterpret_cast<uint2*>(Pl + i4) = make_uint2(lo[0] | (uint32_t)lo[1] << 16, lo[2] | (uint32_t)lo[3] << 16);
+}
+
 __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ part, int nsplit,
                                                         int M, int Mp, int r, int rp, float scale,
                                                         float* __restrict__ P32,
                                                         uint16_t* __restrict__ Ph,
                                                         uint16_t* __restrict__ Pl) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)Mp * rp) return;
-  const int64_t m = idx / rp;
-  const int j = (int)(idx % rp);
-  if (m < M && j < r) {
-    float v = 0.0f;
-    for (int s = 0; s < nsplit; ++s) v += part[(int64_t)s * M * rp + idx];
-    if (P32) P32[m * r + j] = v;
-    const float sv = scale * v;
-    const __bf16 h = (__bf16)sv;
-    Ph[idx] = __builtin_bit_cast(uint16_t, h);
-    if (Pl) Pl[idx] = __builtin_bit_cast(uint16_t, (__bf16)(sv - (float)h));
-  } else {
-    Ph[idx] = 0;
-    if (Pl) Pl[idx] = 0;
+  const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i4 >= (int64_t)Mp * rp) return;
+  const int64_t m = i4 / rp;
+  const int j0 = (int)(i4 % rp);
+  float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (m < M) v = sum_slices(part, nsplit, (int64_t)M * rp, i4);
+  const float vv[4] = {v.x, v.y, v.z, v.w};
+  float sv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bool ok = m < M && j0 + e < r;
+    if (ok && P32) P32[m * r + j0 + e] = vv[e];
+    sv[e] = ok ? scale * vv[e] : 0.0f;
   }
+  store_hi_lo(Ph, Pl, i4, sv);
 }
 
 // part[s][j][c] = sum over rows m of slice s of P[m][j] * Q[m][c],
@@ -564,24 +589,23 @@ __global__ __launch_bounds__(256) void finalize2_kernel(const float* __restrict_
                                                          const float* __restrict__ T,
                                                          uint16_t* __restrict__ Th,
                                                          uint16_t* __restrict__ Tl) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)Mp * rp) return;
-  const int64_t m = idx / rp;
-  const int j = (int)(idx % rp);
-  const bool ok = m < M && j < r;
-  float v = 0.0f;
-  if (ok) {
-    for (int sp = 0; sp < nsplit; ++sp) v += part[(int64_t)sp * M * rp + idx];
-    if (P32) P32[m * r + j] = v;
+  const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i4 >= (int64_t)Mp * rp) return;
+  const int64_t m = i4 / rp;
+  const int j0 = (int)(i4 % rp);
+  float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (m < M) v = sum_slices(part, nsplit, (int64_t)M * rp, i4);
+  const float vv[4] = {v.x, v.y, v.z, v.w};
+  float sv[4], tv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bool ok = m < M && j0 + e < r;
+    if (ok && P32) P32[m * r + j0 + e] = vv[e];
+    sv[e] = ok ? scale * vv[e] : 0.0f;
+    tv[e] = ok ? scale * T[m * r + j0 + e] : 0.0f;
   }
-  const float sv = ok ? scale * v : 0.0f;
-  const __bf16 h = (__bf16)sv;
-  Ph[idx] = __builtin_bit_cast(uint16_t, h);
-  Pl[idx] = __builtin_bit_cast(uint16_t, (__bf16)(sv - (float)h));
-  const float tv = ok ? scale * T[m * r + j] : 0.0f;
-  const __bf16 th = (__bf16)tv;
-  Th[idx] = __builtin_bit_cast(uint16_t, th);
-  Tl[idx] = __builtin_bit_cast(uint16_t, (__bf16)(tv - (float)th));
+  store_hi_lo(Ph, Pl, i4, sv);
+  store_hi_lo(Th, Tl, i4, tv);
 }
 
 // Both adapter-gradient reductions in one launch: dA [r, C1] from partials
@@ -636,7 +660,7 @@ hipError_t launch_proj(const uint16_t* L, const uint16_t* R, int M, int Kr, int 
 
 hipError_t launch_finalize(const float* part, int nsplit, int M, int Mp, int r, int rp, float scale,
                            float* P32, uint16_t* Ph, uint16_t* Pl, hipStream_t s) {
-  const int64_t total = (int64_t)Mp * rp;
+  const int64_t total = (int64_t)Mp * rp / 4;
   hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part,
                      nsplit, M, Mp, r, rp, scale, P32, Ph, Pl);
   return hipGetLastError();
@@ -703,7 +727,7 @@ hipError_t launch_transpose2(const uint16_t* B, const uint16_t* A, int N, int K,
 hipError_t launch_finalize2(const float* part, int nsplit, int M, int Mp, int r, int rp, float scale,
                             float* P32, uint16_t* Ph, uint16_t* Pl, const float* T, uint16_t* Th,
                             uint16_t* Tl, hipStream_t s) {
-  const int64_t total = (int64_t)Mp * rp;
+  const int64_t total = (int64_t)Mp * rp / 4;
   hipLaunchKernelGGL(finalize2_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, nsplit, M,
                      Mp, r, rp, scale, P32, Ph, Pl, T, Th, Tl);
   return hipGetLastError();
