@@ -57,6 +57,13 @@ def test_merge_nf4_dq(N, K, r):
     _check(N, K, r, "nf4", True, seed=N)
 
 
+# K % 64 == 0 runs the MFMA form (64 x 256 tiles, 64-deep rank chunks): ragged
+# rows and columns, odd ranks, a partial last rank chunk, K = 11008
+@pytest.mark.parametrize("N,K,r", [(300, 576, 33), (130, 11008, 100), (64, 320, 200), (17, 64, 1)])
+def test_merge_mfma_tiles(N, K, r):
+    _check(N, K, r, "nf4", True, seed=N + r)
+
+
 @pytest.mark.parametrize("cb,dq", [("int4", False), ("fp4", True), ("nf4", False)])
 def test_merge_other_formats(cb, dq):
     _check(384, 1024, 64, cb, dq, seed=7)
