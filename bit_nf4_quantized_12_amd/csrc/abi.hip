@@ -27,9 +27,16 @@ inline int proj_splits(int64_t M, int64_t Kr) {
   return clampi(cdiv(512, cdiv(M, 64)), 1, std::min<int64_t>(64, max_split));
 }
 inline int grad_splits(int64_t M, int64_t C, int64_t rp) {
-  // ~256 workgroups, each slice at least 8 steps of 64 rows
-  const int64_t wgs = cdiv(C, 128) * cdiv(rp, 64);
-  return clampi(cdiv(256, wgs), 1, std::max<int64_t>(1, cdiv(M, 512)));
+  // The gradient kernel holds one workgroup per CU (128 KB of LDS), so a
+  // launch of w s workgroups takes ceil(w s / 256) rounds of 1/s of the rows
+  // each: pick s (<= 8, each slice at least 8 steps of 64 rows) minimising
+  // ceil(w s / 256) / s; ties go to fewer splits (less partial traffic).
+  const int64_t w = cdiv(C, 128) * cdiv(rp, 64);
+  const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(8, cdiv(M, 512)));
+  int64_t best = 1;
+  for (int64_t sp = 2; sp <= smax; ++sp)
+    if (cdiv(w * sp, 256) * best < cdiv(w * best, 256) * sp) best = sp;
+  return (int)best;
 }
 
 struct Layout {
@@ -43,7 +50,9 @@ struct Layout {
   int ksY = 1, kcY = 0, ksX = 1, kcX = 0;
 };
 
-Layout plan(int64_t M, int64_t N, int64_t K, int64_t r) {
+// r is the total rank (g r_seg for g grouped segments); the dB gradient of
+// grouped linears runs one segment's r_seg columns per workgroup.
+Layout plan(int64_t M, int64_t N, int64_t K, int64_t r, int64_t groups = 1) {
   Layout L;
   const int64_t rp = cdiv(r, 64) * 64;
   // forward
@@ -64,8 +73,9 @@ Layout plan(int64_t M, int64_t N, int64_t K, int64_t r) {
   L.At = o;    o = al256(o + (size_t)K * rp * 2);
   L.partU = o; o = al256(o + (size_t)L.usplit * M * rp * 4);
   L.U32 = o;   o = al256(o + (size_t)M * r * 4);
+  const int64_t rpB = groups > 1 ? r / groups : rp;  // grouped: r_seg, a multiple of 64
   L.sA = grad_splits(M, K, rp);
-  L.sB = grad_splits(M, N, rp);
+  L.sB = grad_splits(M, N, rpB);
   const int64_t Mp = cdiv(M, 64) * 64;
   L.PtH = o;   o = al256(o + (size_t)rp * Mp * 2);
   L.PtL = o;   o = al256(o + (size_t)rp * Mp * 2);
@@ -400,7 +410,7 @@ int fwd_grouped_impl(const WView& W, int64_t g, const void* X, const void* A, co
   if (!Y) return QLORA_ERR_NULL;
   if (!aligned(Y, 16) || (T_save && !aligned(T_save, 4))) return QLORA_ERR_ALIGN;
   const int64_t N = W.N, K = W.K, Ns = N / g;
-  const Layout L = plan(M, N, K, R);
+  const Layout L = plan(M, N, K, R, g);
   if (ws_bytes < L.fwd_total) return QLORA_ERR_WORKSPACE;
   try {
     if (tables_status() != 0) return QLORA_ERR_UNSUPPORTED;
@@ -462,7 +472,7 @@ int bwd_grouped_impl(const WView& W, int64_t g, const void* X, const void* A, co
       (T_saved && !aligned(T_saved, 4)))
     return QLORA_ERR_ALIGN;
   const int64_t N = W.N, K = W.K, Ns = N / g;
-  const Layout L = plan(M, N, K, R);
+  const Layout L = plan(M, N, K, R, g);
   if (ws_bytes < L.bwd_total) return QLORA_ERR_WORKSPACE;
   try {
     if (tables_status() != 0) return QLORA_ERR_UNSUPPORTED;
@@ -729,7 +739,7 @@ size_t qlora_linear_grouped_workspace_bytes(int64_t M, int64_t N, int64_t K, int
   if (groups < 1 || groups > 16 || M < 1 || N < 1 || K < 64 || (K % 64) != 0 || r < 1 || r > 256) return 0;
   if (groups > 1 && (N % groups != 0 || (N / groups) % 256 != 0 || r % 64 != 0)) return 0;
   if (M * std::max(N, K) >= (int64_t(1) << 31)) return 0;
-  const Layout L = plan(M, N, K, groups * r);
+  const Layout L = plan(M, N, K, groups * r, groups);
   return std::max(L.fwd_total, L.bwd_total);
 }
 
