@@ -19,6 +19,13 @@ inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int clampi(int64_t v, int64_t lo, int64_t hi) { return (int)(v < lo ? lo : (v > hi ? hi : v)); }
+// Every [rows, cols] operand of the linear layer is indexed in 32 bits:
+// 64 ceil(M / 64) rows (the padded planes) times max(N, K, 64 ceil(r / 64))
+// elements must stay below 2^31 (so byte offsets stay below 2^32).
+inline bool index_fits(int64_t M, int64_t N, int64_t K, int64_t r) {
+  const int64_t Mp = cdiv(M, 64) * 64, rp = cdiv(r, 64) * 64;
+  return Mp * std::max(std::max(N, K), rp) < (int64_t(1) << 31);
+}
 
 // Reduction splits. Each aims at a few hundred workgroups on 256 CUs.
 inline int proj_splits(int64_t M, int64_t Kr) {
@@ -143,7 +150,7 @@ int check_linear(const WView& W, const void* X, const void* A, const void* B,
   const int64_t N = W.N, K = W.K;
   if (M < 1 || N < 1 || K < 64 || (K % 64) != 0) return QLORA_ERR_SHAPE;
   if (r < 1 || r > 256) return QLORA_ERR_SHAPE;
-  if (M * std::max(N, K) >= (int64_t(1) << 31) || N * K >= (int64_t(1) << 40)) return QLORA_ERR_SHAPE;
+  if (!index_fits(M, N, K, r) || N * K >= (int64_t(1) << 40)) return QLORA_ERR_SHAPE;
   if (!std::isfinite(scale)) return QLORA_ERR_UNSUPPORTED;
   if (!aligned(X, 16) || !aligned(A, 16) || !aligned(B, 16)) return QLORA_ERR_ALIGN;
   if (!ws) return QLORA_ERR_WORKSPACE;
@@ -738,7 +745,7 @@ int qlora_merge_lora(const qlora_4bit_weight* W, const void* A, const void* B, i
 size_t qlora_linear_grouped_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r, int64_t groups) {
   if (groups < 1 || groups > 16 || M < 1 || N < 1 || K < 64 || (K % 64) != 0 || r < 1 || r > 256) return 0;
   if (groups > 1 && (N % groups != 0 || (N / groups) % 256 != 0 || r % 64 != 0)) return 0;
-  if (M * std::max(N, K) >= (int64_t(1) << 31)) return 0;
+  if (!index_fits(M, N, K, groups * r)) return 0;
   const Layout L = plan(M, N, K, groups * r, groups);
   return std::max(L.fwd_total, L.bwd_total);
 }
@@ -763,7 +770,7 @@ int qlora_linear_bwd_grouped(const qlora_4bit_weight* W, int64_t groups, const v
 
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
   if (M < 1 || N < 1 || K < 64 || (K % 64) != 0 || r < 1 || r > 256) return 0;
-  if (M * std::max(N, K) >= (int64_t(1) << 31)) return 0;
+  if (!index_fits(M, N, K, r)) return 0;
   const Layout L = plan(M, N, K, r);
   return std::max(L.fwd_total, L.bwd_total);
 }

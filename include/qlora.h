@@ -131,7 +131,8 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
  * T_save: device float32 [M, r] output, or NULL. ws: device workspace of at
  * least qlora_linear_workspace_bytes(M, N, K, r) bytes, 256-byte aligned.
  * Limits: 1 <= M, 1 <= N, 64 <= K, K % 64 == 0, 1 <= r <= 256, scale finite,
- * M * max(N, K) < 2^31. Errors: NULL, SHAPE, ALIGN, UNSUPPORTED,
+ * Mp * max(N, K, rp) < 2^31 with Mp = 64 ceil(M / 64), rp = 64 ceil(r / 64)
+ * (32-bit indexing of every operand). Errors: NULL, SHAPE, ALIGN, UNSUPPORTED,
  * WORKSPACE, DEVICE. */
 int qlora_linear_fwd(const qlora_nf4_weight* W, const void* X, const void* A,
                      const void* B, int64_t M, int64_t r, float scale, void* Y,

@@ -109,6 +109,14 @@ def test_linear_fwd_validation(lib):
     assert call(args(W=ctypes.byref(w3))) == NULL
     w4 = _w(128, 128, codes=FAKE + 1)
     assert call(args(W=ctypes.byref(w4))) == ALIGN
+    # 32-bit indexing: 64 ceil(M / 64) * max(N, K, 64 ceil(r / 64)) < 2^31
+    wsm = _w(64, 64)
+    mmax = (1 << 31) // 64 - 64                       # the largest multiple of 64 that fits with N = K = 64
+    assert lib.qlora_linear_workspace_bytes(mmax, 64, 64, 64) > 0
+    assert lib.qlora_linear_workspace_bytes(mmax + 1, 64, 64, 64) == 0    # the padded rows reach 2^31
+    assert lib.qlora_linear_workspace_bytes(mmax, 64, 64, 65) == 0        # the padded rank is 128
+    assert call(args(W=ctypes.byref(wsm), M=mmax, r=65)) == SHAPE
+    assert call(args(W=ctypes.byref(wsm), M=mmax + 1, r=8)) == SHAPE
 
 
 def test_linear_bwd_validation(lib):
