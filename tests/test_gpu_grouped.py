@@ -10,6 +10,7 @@ import torch
 import bit_nf4_quantized_12_amd as q
 import oracle
 from bit_nf4_quantized_12_amd import synth
+from tests import oracle_pool
 from tests.parity import assert_close, bf16_bits_to_f32, report
 
 pytestmark = pytest.mark.gpu
@@ -76,3 +77,38 @@ def test_grouped_one_segment_is_the_plain_linear():
 def test_grouped_llama7b_qkv_sampled():
     # q/k/v of a 7B layer: g = 3, Ns = K = 4096, 2048 tokens; outputs checked on the full arrays
     _case(2048, 3, 4096, 4096, 64, seed=6)
+
+
+@pytest.fixture(scope="module")
+def pool():
+    with oracle_pool.make_pool() as p:
+        yield p
+
+
+@pytest.mark.parametrize("g,ns", [(3, 4096), (2, 11008)], ids=["qkv", "gate_up"])
+def test_grouped_llama7b_layer_units_8192_tokens(g, ns, pool):
+    # the decoder-layer units as the benchmark step runs them: 8192 tokens,
+    # r = 64 per segment, K = 4096. Y, T and dX on seeded rows; dA and dB in full.
+    M, K, r = 8192, 4096, 64
+    N = g * ns
+    report(f"grouped parity (sampled rows): M={M} g={g} Ns={ns} K={K} r={r}")
+    case = synth.linear_case(M, N, K, g * r, seed=9, cfg=171)
+    Wt, Xt, At, dYt = (case[k][0].to(DEV) for k in ("W", "X", "A", "dY"))
+    w32, x, a, dy = (case[k][1] for k in ("W", "X", "A", "dY"))
+    bt, b = synth.normal((N, r), 0.02, 9, (171, 0, synth.B_ID))
+    s = 16.0 / r
+    W = q.quantize_weight(Wt)
+    Y, T = q.qlora_linear_fwd_grouped(W, g, Xt, At, bt.to(DEV), s)
+    dX, dA, dB = q.qlora_linear_bwd_grouped(W, g, Xt, At, bt.to(DEV), dYt, T, s)
+    torch.cuda.synchronize()
+    pk, c2, c1 = oracle_pool.quantize_parallel(w32.ravel(), pool)
+    Wo = oracle.bf16_round(oracle.dequant(pk, c2, c1, w32.size)).reshape(N, K)
+    rows = np.random.default_rng(g).choice(M, 96, replace=False)
+    Yr, Tr = oracle.grouped_linear_fwd(x[rows], Wo, a, b, s, g)
+    assert_close(bf16_bits_to_f32(Y)[rows], Yr, "Y")
+    assert_close(T.cpu().numpy()[rows], Tr, "T")
+    dXr, _, _ = oracle.grouped_linear_bwd(x[rows], Wo, a, b, dy[rows], s, g)
+    assert_close(bf16_bits_to_f32(dX)[rows], dXr, "dX")
+    _, dAr, dBr = oracle.grouped_linear_bwd(x, None, a, b, dy, s, g, need_dX=False)
+    assert_close(bf16_bits_to_f32(dA), dAr, "dA")
+    assert_close(bf16_bits_to_f32(dB), dBr, "dB")
