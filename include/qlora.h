@@ -271,8 +271,10 @@ int qlora_linear_bwd_grouped(const qlora_4bit_weight* W, int64_t groups, const v
  * into one dense weight:
  *   out[n][k] = bf16( fp32( W^[n][k] + fp32(scale * sum_j B[n][j] A[j][k]) ) )
  * with W^ the exact float32 dequantised weight of W (any stored format), the
- * sum over j in float32 (ascending j, fused multiply-add), one final
- * rounding to bf16 (nearest even). A [r, K], B [N, r]: device bf16; out:
+ * sum over j in float32 (K % 64 == 0: on the matrix cores, bf16 products
+ * exact, sums in their order; otherwise ascending j with fused multiply-
+ * add; either way within (r + 2) u (|W^| + scale sum_j |B A|) of the exact
+ * value, u = 2^-24), one final rounding to bf16 (nearest even). A [r, K], B [N, r]: device bf16; out:
  * device bf16 [N, K]. 1 <= r <= 256. Errors: NULL, SHAPE, ALIGN,
  * UNSUPPORTED (format or non-finite scale), DEVICE. */
 int qlora_merge_lora(const qlora_4bit_weight* W, const void* A, const void* B, int64_t r,
