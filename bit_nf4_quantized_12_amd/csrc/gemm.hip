@@ -420,13 +420,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 template <int BM, int BN, bool TW, bool LORA, bool VEC, bool ABS>
 hipError_t launch_variant(const GemmParams& p, hipStream_t s) {
   constexpr size_t smem_bytes = 2 * (BM + BN) * 64 * sizeof(uint16_t);
-  static bool configured = false;  // benign race: every thread sets the same value
-  if (!configured) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<BM, BN, TW, LORA, VEC, ABS>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_bytes);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  static std::atomic<uint32_t> lds_ok{0};
+  const hipError_t le =
+      ensure_lds(reinterpret_cast<const void*>(&gemm_kernel<BM, BN, TW, LORA, VEC, ABS>), (int)smem_bytes, lds_ok);
+  if (le != hipSuccess) return le;
   const int tiles = ((p.Nout + BN - 1) / BN) * ((p.M + BM - 1) / BM);
   const int grid = 8 * ((tiles * p.ksplit + 7) / 8);
   hipLaunchKernelGGL((gemm_kernel<BM, BN, TW, LORA, VEC, ABS>), dim3(grid), dim3(NT), smem_bytes, s, p);

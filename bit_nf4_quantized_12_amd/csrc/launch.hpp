@@ -1,9 +1,25 @@
 // Host-side launchers of the library's kernels (one per .hip file).
 #pragma once
 
+#include <atomic>
+
 #include "common.hpp"
 
 namespace qlora {
+
+// Opt kernel fn in to `bytes` of dynamic LDS (above the default 64 KB) on
+// the current device. The attribute is per device, so `done` keeps one bit
+// per device (devices past 31 set it on every call).
+inline hipError_t ensure_lds(const void* fn, int bytes, std::atomic<uint32_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint32_t bit = dev < 32 ? (1u << dev) : 0u;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 struct GemmParams {
   const uint16_t* act;     // [M, Kred] bf16, row pitch Kred

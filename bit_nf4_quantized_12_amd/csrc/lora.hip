@@ -685,17 +685,11 @@ hipError_t launch_grad_reduce(const float* part, int nsplit, int r, int rp, int 
 hipError_t launch_grad_tr(const uint16_t* Ph, const uint16_t* Pl, const uint16_t* Q, int M, int Mp, int C,
                           int rp, int nsplit, bool trans, float* part, hipStream_t s, int segC, int rseg) {
   if (!segC) rseg = rp;
-  static bool configured = false;  // benign race: every thread sets the same value
   const size_t smem = (size_t)GT_STAGES * GT_STAGE * sizeof(uint16_t);
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&grad_tr_kernel<false>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&grad_tr_kernel<true>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  static std::atomic<uint32_t> lds_ok[2];
+  hipError_t e = ensure_lds(reinterpret_cast<const void*>(&grad_tr_kernel<false>), (int)smem, lds_ok[0]);
+  if (e == hipSuccess) e = ensure_lds(reinterpret_cast<const void*>(&grad_tr_kernel<true>), (int)smem, lds_ok[1]);
+  if (e != hipSuccess) return e;
   const int mchunk = ((Mp + nsplit - 1) / nsplit + 63) / 64 * 64;
   dim3 grid((C + 127) / 128, nsplit, rseg / 64);
   if (trans)

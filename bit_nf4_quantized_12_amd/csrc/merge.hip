@@ -227,13 +227,9 @@ template <bool ABS>
 static hipError_t launch_merge_mfma(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* absmax,
                                     int codebook, const uint16_t* A, const uint16_t* B, int N, int K, int r,
                                     float scale, uint16_t* out, hipStream_t s) {
-  static bool configured = false;  // more than 64 KB of LDS needs an opt-in
-  if (!configured) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&merge_mfma_kernel<ABS>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, MM_LDS);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  static std::atomic<uint32_t> lds_ok{0};  // more than 64 KB of LDS needs an opt-in
+  const hipError_t e = ensure_lds(reinterpret_cast<const void*>(&merge_mfma_kernel<ABS>), MM_LDS, lds_ok);
+  if (e != hipSuccess) return e;
   const dim3 grid((K + MM_COLS - 1) / MM_COLS, (N + MM_ROWS - 1) / MM_ROWS);
   hipLaunchKernelGGL(merge_mfma_kernel<ABS>, grid, dim3(MM_NT), MM_LDS, s, codes, c2, c1, absmax, A, B, N, K, r, scale,
                      out, host_levels(codebook));
