@@ -147,6 +147,40 @@ def _need(t, dtype, name):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _same_device(dev, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other operands on {dev}")
+
+
+def _buf(t, shape, dtype, dev, name):
+    """A new tensor of this shape, or the caller's one after checking it (the
+    library writes shape[0] * shape[1] elements through its pointer)."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    _need(t, dtype, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    _same_device(dev, **{name: t})
+    return t
+
+
+def _check_stored(n, codes, consts, c1, double_quant, dev):
+    """The stored buffers of n weights hold what the library reads."""
+    nb = -(-n // 64)
+    need = [("codes", codes, -(-n // 2)), ("block constants", consts, nb)]
+    if double_quant:
+        need.append(("c1", c1, -(-nb // 256)))
+    for name, t, cnt in need:
+        if t.numel() < cnt:
+            raise ValueError(f"{name} holds {t.numel()} elements, {n} weights need {cnt}")
+        _same_device(dev, **{name: t})
+
+
+def _check_weight(W, dev):
+    _check_stored(W.rows * W.cols, W.codes, W.c2, W.c1, W.double_quant, dev)
+
+
 NF4Weight = namedtuple("NF4Weight", ["codes", "c2", "c1", "rows", "cols", "codebook", "double_quant"],
                        defaults=("nf4", True))
 NF4Weight.__doc__ = (
@@ -233,8 +267,8 @@ def qlora_dequant_4bit(codes, consts, c1, n, codebook="nf4", double_quant=True, 
     code = {torch.float32: QLORA_F32, torch.bfloat16: QLORA_BF16}.get(dtype)
     if code is None:
         raise TypeError("dtype must be float32 or bfloat16")
-    if out is None:
-        out = torch.empty(n, dtype=dtype, device=codes.device)
+    _check_stored(n, codes, consts, c1, double_quant, codes.device)
+    out = _buf(out, (n,), dtype, codes.device, "out")
     _check(load_library().qlora_dequant_4bit(_ptr(codes), _ptr(consts), _ptr(c1) if double_quant else None, n,
                                              _codebook_id(codebook), 1 if double_quant else 0, code,
                                              _ptr(out), _stream(codes.device)))
@@ -268,8 +302,8 @@ def qlora_dequant(codes, c2, c1, n, dtype=torch.float32, out=None):
     code = {torch.float32: QLORA_F32, torch.bfloat16: QLORA_BF16}.get(dtype)
     if code is None:
         raise TypeError("dtype must be float32 or bfloat16")
-    if out is None:
-        out = torch.empty(n, dtype=dtype, device=codes.device)
+    _check_stored(n, codes, c2, c1, True, codes.device)
+    out = _buf(out, (n,), dtype, codes.device, "out")
     _check(load_library().qlora_dequant(_ptr(codes), _ptr(c2), _ptr(c1), n, code, _ptr(out),
                                         _stream(codes.device)))
     return out
@@ -281,8 +315,8 @@ def qlora_nf4_matmul(W, act, transposed=False, out=None):
     M = act.shape[0]
     if act.shape[1] != (W.rows if transposed else W.cols):
         raise ValueError("act has the wrong number of columns")
-    if out is None:
-        out = torch.empty((M, W.cols if transposed else W.rows), dtype=torch.bfloat16, device=act.device)
+    _check_weight(W, act.device)
+    out = _buf(out, (M, W.cols if transposed else W.rows), torch.bfloat16, act.device, "out")
     w, sfx = _weight_struct(W)
     fn = load_library().qlora_nf4_matmul if not sfx else load_library().qlora_4bit_matmul
     _check(fn(ctypes.byref(w), _ptr(act), M, 1 if transposed else 0, _ptr(out), _stream(act.device)))
@@ -334,12 +368,10 @@ def qlora_linear_fwd(W, X, A, B, scale, save_T=True, Y=None, T=None, workspace=N
     if K != W.cols or A.shape[1] != K or B.shape != (W.rows, r):
         raise ValueError("shape mismatch: X [M, K], A [r, K], B [N, r], W [N, K]")
     dev = X.device
-    if Y is None:
-        Y = torch.empty((M, W.rows), dtype=torch.bfloat16, device=dev)
-    if save_T and T is None:
-        T = torch.empty((M, r), dtype=torch.float32, device=dev)
-    if not save_T:
-        T = None
+    _same_device(dev, A=A, B=B)
+    _check_weight(W, dev)
+    Y = _buf(Y, (M, W.rows), torch.bfloat16, dev, "Y")
+    T = _buf(T, (M, r), torch.float32, dev, "T") if save_T else None
     ws = _workspace(M, W.rows, K, r, dev, workspace)
     w, sfx = _weight_struct(W)
     fn = getattr(load_library(), "qlora_linear_fwd" + sfx)
@@ -360,15 +392,14 @@ def qlora_linear_bwd(W, X, A, B, dY, T, scale, need_dX=True, dX=None, dA=None, d
     N = W.rows
     if dY.shape != (M, N) or K != W.cols or A.shape[1] != K or B.shape != (N, r):
         raise ValueError("shape mismatch")
+    if T is not None and tuple(T.shape) != (M, r):
+        raise ValueError(f"T must have shape {(M, r)}")
     dev = X.device
-    if need_dX and dX is None:
-        dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-    if not need_dX:
-        dX = None
-    if dA is None:
-        dA = torch.empty((r, K), dtype=torch.bfloat16, device=dev)
-    if dB is None:
-        dB = torch.empty((N, r), dtype=torch.bfloat16, device=dev)
+    _same_device(dev, A=A, B=B, dY=dY, T=T)
+    _check_weight(W, dev)
+    dX = _buf(dX, (M, K), torch.bfloat16, dev, "dX") if need_dX else None
+    dA = _buf(dA, (r, K), torch.bfloat16, dev, "dA")
+    dB = _buf(dB, (N, r), torch.bfloat16, dev, "dB")
     ws = _workspace(M, N, K, r, dev, workspace)
     w, sfx = _weight_struct(W)
     fn = getattr(load_library(), "qlora_linear_bwd" + sfx)
@@ -455,12 +486,10 @@ def qlora_linear_fwd_grouped(W, groups, X, A, B, scale, save_T=True, Y=None, T=N
     if A.shape != (g * r, K) or B.shape != (W.rows, r) or W.cols != K:
         raise ValueError("shape mismatch: X [M, K], A [g r, K], B [g Ns, r], W [g Ns, K]")
     dev = X.device
-    if Y is None:
-        Y = torch.empty((M, W.rows), dtype=torch.bfloat16, device=dev)
-    if save_T and T is None:
-        T = torch.empty((M, g * r), dtype=torch.float32, device=dev)
-    if not save_T:
-        T = None
+    _same_device(dev, A=A, B=B)
+    _check_weight(W, dev)
+    Y = _buf(Y, (M, W.rows), torch.bfloat16, dev, "Y")
+    T = _buf(T, (M, g * r), torch.float32, dev, "T") if save_T else None
     need = qlora_linear_grouped_workspace_bytes(M, W.rows, K, r, g)
     ws = workspace if workspace is not None and workspace.numel() >= need else \
         torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
@@ -484,15 +513,14 @@ def qlora_linear_bwd_grouped(W, groups, X, A, B, dY, T, scale, need_dX=True, dX=
     N = W.rows
     if dY.shape != (M, N) or A.shape != (g * r, K) or B.shape != (N, r) or W.cols != K:
         raise ValueError("shape mismatch")
+    if T is not None and tuple(T.shape) != (M, g * r):
+        raise ValueError(f"T must have shape {(M, g * r)}")
     dev = X.device
-    if need_dX and dX is None:
-        dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-    if not need_dX:
-        dX = None
-    if dA is None:
-        dA = torch.empty((g * r, K), dtype=torch.bfloat16, device=dev)
-    if dB is None:
-        dB = torch.empty((N, r), dtype=torch.bfloat16, device=dev)
+    _same_device(dev, A=A, B=B, dY=dY, T=T)
+    _check_weight(W, dev)
+    dX = _buf(dX, (M, K), torch.bfloat16, dev, "dX") if need_dX else None
+    dA = _buf(dA, (g * r, K), torch.bfloat16, dev, "dA")
+    dB = _buf(dB, (N, r), torch.bfloat16, dev, "dB")
     need = qlora_linear_grouped_workspace_bytes(M, N, K, r, g)
     ws = workspace if workspace is not None and workspace.numel() >= need else \
         torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
@@ -510,8 +538,9 @@ def qlora_merge_lora(W, A, B, scale, out=None):
     r = A.shape[0]
     if A.shape != (r, W.cols) or B.shape != (W.rows, r):
         raise ValueError("shape mismatch: A [r, K], B [N, r], W [N, K]")
-    if out is None:
-        out = torch.empty((W.rows, W.cols), dtype=torch.bfloat16, device=A.device)
+    _same_device(A.device, B=B)
+    _check_weight(W, A.device)
+    out = _buf(out, (W.rows, W.cols), torch.bfloat16, A.device, "out")
     w = _weight4_struct(W)
     _check(load_library().qlora_merge_lora(ctypes.byref(w), _ptr(A), _ptr(B), r, float(scale), _ptr(out),
                                            _stream(A.device)))

@@ -164,3 +164,27 @@ def test_65b_layer_linears_8192_tokens(N, K, pool):
     # the block absmax); Y and dX on 256 seeded rows, dA and dB in full
     rows = np.random.default_rng(N + 3 * K).choice(8192, 256, replace=False)
     run_case(8192, N, K, 64, 16.0, cfg=4, rows=rows, w_dist="student_t", pool=pool)
+
+
+def test_binding_rejects_malformed_buffers():
+    # caught in the binding, before anything is launched
+    case = synth.linear_case(16, 256, 256, 8, cfg=107)
+    Wt, Xt, At, Bt, dYt = (case[k][0].to(DEV) for k in ("W", "X", "A", "B", "dY"))
+    W = q.quantize_weight(Wt)
+    with pytest.raises(ValueError):
+        q.qlora_linear_fwd(W, Xt, At, Bt, 1.0, Y=torch.empty(16, 255, dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ValueError):
+        q.qlora_linear_fwd(W._replace(codes=W.codes[:1000]), Xt, At, Bt, 1.0)
+    with pytest.raises(ValueError):
+        q.qlora_linear_fwd(W._replace(c1=W.c1[:0]), Xt, At, Bt, 1.0)
+    with pytest.raises(ValueError):
+        q.qlora_linear_bwd(W, Xt, At, Bt, dYt, torch.empty(16, 7, device=DEV), 1.0)
+    with pytest.raises(TypeError):
+        q.qlora_linear_bwd(W, Xt, At, Bt, dYt, None, 1.0, dA=torch.empty(8, 256, dtype=torch.float32, device=DEV))
+    with pytest.raises(ValueError):
+        q.qlora_dequant(W.codes, W.c2, W.c1, 256 * 256 + 64)
+    with pytest.raises(ValueError):
+        q.qlora_merge_lora(W, At, Bt, 1.0, out=torch.empty(256 * 256, dtype=torch.bfloat16, device=DEV))
+    Y, _ = q.qlora_linear_fwd(W, Xt, At, Bt, 1.0)  # the well-formed call still runs
+    torch.cuda.synchronize()
+    assert Y.shape == (16, 256)
