@@ -645,12 +645,15 @@ int qlora_quantize_nf4_dq(const void* w_bf16, int64_t n, uint8_t* codes, uint8_t
   return qlora_quantize_4bit(w_bf16, n, kNF4, 1, codes, c2_fp8, c1, stream);
 }
 
+// one dequantisation workgroup per 8192 weights, at most 2^31 - 1 of them
+constexpr int64_t kMaxDequant = (int64_t)1 << 43;
+
 int qlora_dequant_4bit(const uint8_t* codes, const void* consts, const float* c1, int64_t n, int codebook,
                        int double_quant, int out_dtype, void* out, void* stream) {
   const int f = check_format(codebook, double_quant);
   if (f != QLORA_OK) return f;
   if (!codes || !consts || (double_quant && !c1) || !out) return QLORA_ERR_NULL;
-  if (n < 1) return QLORA_ERR_SHAPE;
+  if (n < 1 || n > kMaxDequant) return QLORA_ERR_SHAPE;
   if (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16) return QLORA_ERR_UNSUPPORTED;
   if (!aligned(codes, 16) || !aligned(consts, 16) || (double_quant && !aligned(c1, 4)) || !aligned(out, 16))
     return QLORA_ERR_ALIGN;

@@ -97,8 +97,8 @@ int qlora_quantize_nf4_dq(const void* w_bf16, int64_t n, uint8_t* codes,
  * is dequantised to BFloat16 whenever it is used. out_dtype QLORA_F32 writes
  * W^ (float32, bit-exact per the formula above); QLORA_BF16 writes W~.
  * codes / c2_fp8 / c1: device inputs; out: device output of n elements,
- * 16-byte aligned. Errors: NULL, SHAPE (n < 1), ALIGN, UNSUPPORTED (dtype),
- * DEVICE. */
+ * 16-byte aligned. Errors: NULL, SHAPE (n < 1 or n > 2^43), ALIGN,
+ * UNSUPPORTED (dtype), DEVICE. */
 int qlora_dequant(const uint8_t* codes, const uint8_t* c2_fp8, const float* c1,
                   int64_t n, int out_dtype, void* out, void* stream);
 
@@ -216,8 +216,8 @@ int qlora_quantize_4bit_batch(int count, const void* const* w_bf16, const int64_
 
 /* Dequantise n weights of a stored 4-bit format to float32 (W^) or bf16
  * (W~): [P2] "Method". Inputs as written by qlora_quantize_4bit with the
- * same codebook and double_quant. Errors: NULL, SHAPE, ALIGN, UNSUPPORTED,
- * DEVICE. */
+ * same codebook and double_quant. Errors: NULL, SHAPE (n < 1 or n > 2^43),
+ * ALIGN, UNSUPPORTED, DEVICE. */
 int qlora_dequant_4bit(const uint8_t* codes, const void* consts, const float* c1, int64_t n,
                        int codebook, int double_quant, int out_dtype, void* out, void* stream);
 

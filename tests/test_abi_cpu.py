@@ -65,6 +65,8 @@ def test_dequant_validation(lib):
     f = lib.qlora_dequant
     assert f(None, FAKE, FAKE, 64, 0, FAKE, None) == NULL
     assert f(FAKE, FAKE, FAKE, 0, 0, FAKE, None) == SHAPE
+    # one workgroup per 8192 weights: at most 2^43 weights per call
+    assert f(FAKE, FAKE, FAKE, (1 << 43) + 1, 0, FAKE, None) == SHAPE
     assert f(FAKE, FAKE, FAKE, 64, 7, FAKE, None) == UNSUPPORTED
     assert f(FAKE, FAKE, FAKE, 64, 0, FAKE + 4, None) == ALIGN
 
@@ -179,6 +181,7 @@ def test_dequant_4bit_validation(lib):
     assert f(FAKE, FAKE, None, 64, 1, 1, 0, FAKE, None) == NULL
     assert f(FAKE, None, None, 64, 1, 0, 0, FAKE, None) == NULL
     assert f(FAKE, FAKE, None, 0, 1, 0, 0, FAKE, None) == SHAPE
+    assert f(FAKE, FAKE, None, (1 << 43) + 1, 1, 0, 0, FAKE, None) == SHAPE
     assert f(FAKE, FAKE, None, 64, 1, 0, 9, FAKE, None) == UNSUPPORTED
     assert f(FAKE, FAKE + 8, None, 64, 1, 0, 0, FAKE, None) == ALIGN
 
