@@ -692,7 +692,7 @@ int qlora_4bit_matmul(const qlora_4bit_weight* W, const void* act, int64_t M, in
 int qlora_adamw_step(float* param_f32, void* param_bf16, const void* grad_bf16, float* m, float* v,
                      int64_t n, const qlora_adamw_params* h, void* stream) {
   if (!param_f32 || !grad_bf16 || !m || !v || !h) return QLORA_ERR_NULL;
-  if (n < 1) return QLORA_ERR_SHAPE;
+  if (n < 1 || n > ((int64_t)1 << 40)) return QLORA_ERR_SHAPE;  // one workgroup per 1024 parameters
   if (!aligned(param_f32, 16) || !aligned(grad_bf16, 16) || !aligned(m, 16) || !aligned(v, 16) ||
       (param_bf16 && !aligned(param_bf16, 16)))
     return QLORA_ERR_ALIGN;

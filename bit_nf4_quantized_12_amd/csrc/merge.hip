@@ -16,6 +16,11 @@
 // general form serves any K; merge_mfma_kernel below serves K % 64 == 0.
 #include "launch.hpp"
 
+// W^ and scale * (B A) are each rounded to float32 before their sum:
+// contraction into FMAs is off for the operators written in this file; the
+// rank-r sums use explicit FMAs or MFMA.
+#pragma clang fp contract(off)
+
 namespace qlora {
 namespace {
 
@@ -71,8 +76,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint8_t* __restrict__ 
     if (n >= N) break;
     const int64_t e = (int64_t)n * K + k;
     const uint32_t code = (codes[e >> 1] >> (4 * (e & 1))) & 15u;
-    const float w = __fmul_rn(sq[code], block_const<ABS>(c2, c1, absmax, e >> 6));
-    const __bf16 h = (__bf16)__fadd_rn(w, __fmul_rn(scale, acc[i]));
+    const float w = sq[code] * block_const<ABS>(c2, c1, absmax, e >> 6);
+    const __bf16 h = (__bf16)(w + scale * acc[i]);
     out[e] = __builtin_bit_cast(uint16_t, h);
   }
 }
@@ -198,7 +203,7 @@ __global__ __launch_bounds__(MM_NT) __attribute__((amdgpu_waves_per_eu(4))) void
   for (int t = 0; t < 8; ++t)
 #pragma unroll
     for (int v = 0; v < 4; ++v)
-      sOut[(wr + 4 * (l >> 4) + v) * MM_OS + wc + 16 * t + (l & 15)] = __fmul_rn(scale, acc[t][v]);
+      sOut[(wr + 4 * (l >> 4) + v) * MM_OS + wc + 16 * t + (l & 15)] = scale * acc[t][v];
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < MM_ITEMS; ++i) {
@@ -209,13 +214,13 @@ __global__ __launch_bounds__(MM_NT) __attribute__((amdgpu_waves_per_eu(4))) void
     const float4 p0 = *reinterpret_cast<const float4*>(sOut + row * MM_OS + 8 * (item & 31));
     const float4 p1 = *reinterpret_cast<const float4*>(sOut + row * MM_OS + 8 * (item & 31) + 4);
     const float lo[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-    const float cb = ABS ? craw[i] : __fmul_rn(e4m3_value(c2b[i]), g1[i]);
+    const float cb = ABS ? craw[i] : e4m3_value(c2b[i]) * g1[i];
     uint32_t hw[4];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const float w0 = __fmul_rn(sq[(cw[i] >> (8 * h)) & 15u], cb);
-      const float w1 = __fmul_rn(sq[(cw[i] >> (8 * h + 4)) & 15u], cb);
-      hw[h] = pack_bf16(__fadd_rn(w0, lo[2 * h]), __fadd_rn(w1, lo[2 * h + 1]));
+      const float w0 = sq[(cw[i] >> (8 * h)) & 15u] * cb;
+      const float w1 = sq[(cw[i] >> (8 * h + 4)) & 15u] * cb;
+      hw[h] = pack_bf16(w0 + lo[2 * h], w1 + lo[2 * h + 1]);
     }
     *reinterpret_cast<uint4*>(out + (int64_t)n * K + kk) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
   }

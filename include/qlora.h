@@ -312,8 +312,8 @@ typedef struct {
  * receiving bf16(updated weight) for the next forward, or NULL. grad_bf16:
  * bf16 gradient [n]. m, v: float32 moments [n] (updated; zero before step
  * 1). All 16-byte aligned; device or pinned host memory; the arrays must not
- * overlap. Errors: NULL, SHAPE (n < 1), ALIGN, UNSUPPORTED (a parameter out of
- * range, or memory that is neither device nor pinned host), DEVICE. */
+ * overlap. Errors: NULL, SHAPE (n < 1 or n > 2^40), ALIGN, UNSUPPORTED (a
+ * parameter out of range, or memory that is neither device nor pinned host), DEVICE. */
 int qlora_adamw_step(float* param_f32, void* param_bf16, const void* grad_bf16, float* m,
                      float* v, int64_t n, const qlora_adamw_params* h, void* stream);
 

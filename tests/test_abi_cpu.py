@@ -216,6 +216,8 @@ def test_adamw_validation(lib):
     assert f(None, None, FAKE, FAKE, FAKE, 64, h, None) == NULL
     assert f(FAKE, None, FAKE, FAKE, FAKE, 64, None, None) == NULL
     assert f(FAKE, None, FAKE, FAKE, FAKE, 0, h, None) == SHAPE
+    # one workgroup per 1024 parameters: at most 2^40 per call
+    assert f(FAKE, None, FAKE, FAKE, FAKE, (1 << 40) + 1, h, None) == SHAPE
     assert f(FAKE + 4, None, FAKE, FAKE, FAKE, 64, h, None) == ALIGN
     assert f(FAKE, FAKE + 2, FAKE, FAKE, FAKE, 64, h, None) == ALIGN
     for bad in (q._AdamWParams(-1.0, 0.9, 0.999, 1e-8, 0.0, 1), q._AdamWParams(1e-3, 1.0, 0.999, 1e-8, 0.0, 1),
