@@ -31,13 +31,15 @@ enum Codebook { kNF4 = 0, kInt4 = 1, kFP4 = 2, kNumCodebooks = 3 };
 // 2 * scale equal cells (at most 32); each cell holds at most one decision
 // threshold (the fp32 value T with: code > j  <=>  x > T_j), so
 //   code(x) = base[cell(x)] + (x > thr[cell(x)]),
-//   cell(x) = min(trunc(fma(x, scale, scale)), last).
-// Cells without a threshold carry thr = +2 (never exceeded).
+//   cell(x) = trunc(fma(x, scale, scale)),
+// which is 2 * scale exactly for x = 1: that entry is the code of x = 1
+// (no clamp needed for |x| <= 1). Cells without a threshold carry thr = +2
+// (never exceeded).
+constexpr int kQuantCells = 32;
 struct QuantTable {
-  float thr[32];
-  int32_t base[32];
+  float thr[kQuantCells + 1];
+  int32_t base[kQuantCells + 1];
   float scale;
-  int32_t last;
 };
 
 // Host side (tables.hip). Built once, immutable afterwards.

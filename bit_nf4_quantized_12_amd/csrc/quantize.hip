@@ -48,9 +48,9 @@ __device__ __forceinline__ float div_block(float w, float c, float r, bool fast)
   return w / c;
 }
 
-__device__ __forceinline__ uint32_t nearest_code(float x, const float2* __restrict__ tab, float scale, int last) {
-  int cell = (int)__builtin_fmaf(x, scale, scale);
-  cell = cell > last ? last : cell;
+// |x| <= 1, so the cell is in [0, 2 scale] (a NaN converts to cell 0)
+__device__ __forceinline__ uint32_t nearest_code(float x, const float2* __restrict__ tab, float scale) {
+  const int cell = (int)__builtin_fmaf(x, scale, scale);
   const float2 t = tab[cell];
   return (uint32_t)__float_as_int(t.y) + (x > t.x ? 1u : 0u);
 }
@@ -68,11 +68,11 @@ __device__ __forceinline__ uint32_t e4m3_code(float rho) {
 }
 
 __global__ __launch_bounds__(256) void quantize_kernel(QuantBatch bt, QuantTable qt) {
-  __shared__ float2 s_tab[32];
+  __shared__ float2 s_tab[kQuantCells + 1];
   __shared__ float s_wmax[4];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  if (tid < 32) s_tab[tid] = make_float2(qt.thr[tid], __int_as_float(qt.base[tid]));
+  if (tid <= kQuantCells) s_tab[tid] = make_float2(qt.thr[tid], __int_as_float(qt.base[tid]));
 
   // this workgroup's tensor (uniform scan over at most kQuantBatch entries)
   // and its group within that tensor
@@ -127,16 +127,20 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantBatch bt, QuantTable
     bmax[j] = m;
     gmax = fmaxf(gmax, m);
 
-    uint32_t word = 0x77777777u;  // an all-zero block maps to the exact zero
-    if (m > 0.0f) {
-      const bool fast = m >= 0x1p-100f && m <= 0x1p100f;
-      const float r = 1.0f / m;
-      word = 0;
+    // an all-zero block is divided by 1: its weights are +-0 and map to the
+    // exact zero like any x = 0
+    const float md = m > 0.0f ? m : 1.0f;
+    const bool fast = md >= 0x1p-100f && md <= 0x1p100f;
+    const float r = 1.0f / md;
+    uint32_t word = 0;
+    if (__all(fast)) {
+      // every block of the wave in range (wave-uniform branch): the
+      // straight-line correctly rounded quotient
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float x = div_block(f[i], m, r, fast);
-        word |= nearest_code(x, s_tab, qt.scale, qt.last) << (4 * i);
-      }
+      for (int i = 0; i < 8; ++i) word |= nearest_code(div_block(f[i], md, r, true), s_tab, qt.scale) << (4 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) word |= nearest_code(div_block(f[i], md, r, fast), s_tab, qt.scale) << (4 * i);
     }
     if (full || e + 8 <= n) {
       __builtin_nontemporal_store(word, reinterpret_cast<uint32_t*>(codes + (e >> 1)));

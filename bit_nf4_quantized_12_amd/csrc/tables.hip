@@ -98,9 +98,10 @@ int build_search(const Levels& lv, double scale, QuantTable& qt) {
   float T[15];
   for (int j = 0; j < 15; ++j) T[j] = round_down_f32(((double)lv.q[j] + (double)lv.q[j + 1]) * 0.5);
   const int cells = (int)std::lround(2.0 * scale);
-  if (cells > 32 || std::fabs(2.0 * scale - cells) > 0.0) return 1;
+  if (cells > kQuantCells || std::fabs(2.0 * scale - cells) > 0.0) return 1;
   int bad = 0;
-  for (int c = 0; c < cells; ++c) {
+  // entry `cells` is the cell of x = 1 alone (lo = 1)
+  for (int c = 0; c <= cells; ++c) {
     const double lo = c / scale - 1.0, hi = (c + 1) / scale - 1.0;
     int base = 0, inside = 0;
     float thr = 2.0f;
@@ -113,7 +114,7 @@ int build_search(const Levels& lv, double scale, QuantTable& qt) {
     qt.thr[c] = thr;
     qt.base[c] = base;
   }
-  for (int c = cells; c < 32; ++c) { qt.thr[c] = 2.0f; qt.base[c] = 0; }
+  for (int c = cells + 1; c <= kQuantCells; ++c) { qt.thr[c] = 2.0f; qt.base[c] = 0; }
   // cell(x) is computed as trunc(fma(x, scale, scale)); its rounding can move
   // an x lying within ~2^-23 of a cell edge into the neighbouring cell. That
   // is harmless unless a threshold itself lies that close to an edge.
@@ -123,7 +124,6 @@ int build_search(const Levels& lv, double scale, QuantTable& qt) {
       if (std::fabs((double)T[j] - (k / scale - 1.0)) <= 0x1p-20) bad = 1;
   }
   qt.scale = (float)scale;
-  qt.last = cells - 1;
   return bad;
 }
 
