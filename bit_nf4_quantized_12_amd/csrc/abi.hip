@@ -590,7 +590,8 @@ int qlora_quantize_4bit(const void* w_bf16, int64_t n, int codebook, int double_
   const int f = check_format(codebook, double_quant);
   if (f != QLORA_OK) return f;
   if (!w_bf16 || !codes || !consts || (double_quant && !c1)) return QLORA_ERR_NULL;
-  if (n < 1) return QLORA_ERR_SHAPE;
+  // one workgroup per 16384-weight group, fewer than 2^31 of them
+  if (n < 1 || cdiv(n, kGroup) >= (int64_t(1) << 31)) return QLORA_ERR_SHAPE;
   if (!aligned(w_bf16, 16) || !aligned(codes, 16) || !aligned(consts, 16) || (double_quant && !aligned(c1, 4)))
     return QLORA_ERR_ALIGN;
   try {

@@ -89,7 +89,8 @@ int qlora_nf4_levels(float out[16]);
  * w_bf16: device, n bf16 (16-byte aligned). codes / c2_fp8 / c1: device
  * outputs sized as in the stored format (codes and c2 16-byte aligned,
  * c1 4-byte aligned). Weights must be finite (non-finite input gives
- * unspecified codes). Errors: NULL, SHAPE (n < 1), ALIGN, DEVICE. */
+ * unspecified codes). Errors: NULL, SHAPE (n < 1 or n > 2^45 - 2^14), ALIGN,
+ * DEVICE. */
 int qlora_quantize_nf4_dq(const void* w_bf16, int64_t n, uint8_t* codes,
                           uint8_t* c2_fp8, float* c1, void* stream);
 
@@ -198,8 +199,8 @@ int qlora_levels(int codebook, float out[16]);
  * with the data type's levels. consts: device output, uint8[ceil(n/64)] (c2)
  * or float[ceil(n/64)] (absmax); c1: device output float[ceil(ceil(n/64)/256)]
  * when double_quant, else ignored. Alignment: w, codes, consts 16 bytes, c1
- * 4 bytes. Errors: NULL, SHAPE (n < 1), ALIGN, UNSUPPORTED (codebook or
- * double_quant out of range), DEVICE. */
+ * 4 bytes. Errors: NULL, SHAPE (n < 1 or n > 2^45 - 2^14), ALIGN,
+ * UNSUPPORTED (codebook or double_quant out of range), DEVICE. */
 int qlora_quantize_4bit(const void* w_bf16, int64_t n, int codebook, int double_quant,
                         uint8_t* codes, void* consts, float* c1, void* stream);
 

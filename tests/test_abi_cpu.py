@@ -56,6 +56,7 @@ def test_quantize_validation(lib):
     assert f(FAKE, 64, None, FAKE, FAKE, None) == NULL
     assert f(FAKE, 0, FAKE, FAKE, FAKE, None) == SHAPE
     assert f(FAKE, -5, FAKE, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, (1 << 45) - (1 << 14) + 1, FAKE, FAKE, FAKE, None) == SHAPE
     assert f(FAKE + 2, 64, FAKE, FAKE, FAKE, None) == ALIGN
     assert f(FAKE, 64, FAKE + 8, FAKE, FAKE, None) == ALIGN
     assert f(FAKE, 64, FAKE, FAKE, FAKE + 1, None) == ALIGN
@@ -171,6 +172,8 @@ def test_quantize_4bit_validation(lib):
     assert f(FAKE, 64, 1, 0, FAKE, None, None, None) == NULL
     assert f(FAKE, 64, 1, 1, FAKE, FAKE, None, None) == NULL     # c1 needed with double quantisation
     assert f(FAKE, 0, 2, 0, FAKE, FAKE, None, None) == SHAPE
+    # one workgroup per 16384 weights, fewer than 2^31 workgroups
+    assert f(FAKE, (1 << 45) - (1 << 14) + 1, 2, 0, FAKE, FAKE, None, None) == SHAPE
     assert f(FAKE, 64, 2, 0, FAKE, FAKE + 4, None, None) == ALIGN
     assert f(FAKE, 64, 2, 1, FAKE, FAKE, FAKE + 2, None) == ALIGN
 
