@@ -72,7 +72,8 @@ def _run(n, steps, placement, seed=0, hp=HP):
     return history
 
 
-@pytest.mark.parametrize("n", [1, 7, 8, 9, 1000, 65536 + 5, 1_000_003])
+# 1024-parameter boundaries: one workgroup each
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 1000, 1023, 1024, 1025, 3 * 1024 + 3, 65536 + 5, 1_000_003])
 def test_device_state(n):
     _run(n, 4, "device", seed=n)
 

@@ -47,7 +47,9 @@ def test_single_linear_weight_256x256():
     _check(t, w.ravel(), "256x256 N(0,0.02)")
 
 
-@pytest.mark.parametrize("n", [1, 2, 7, 8, 63, 64, 65, 1000, 16383, 16384, 16385, 100003, 3 * 16384 + 77])
+# 8192-weight boundaries: one dequantisation workgroup run each
+@pytest.mark.parametrize("n", [1, 2, 7, 8, 63, 64, 65, 1000, 8191, 8192, 8193, 3 * 8192 + 8, 16383, 16384,
+                               16385, 100003, 3 * 16384 + 77])
 def test_ragged_lengths(n):
     t, w = synth.normal((n,), 0.5, 0, (90, n, 0))
     _check(t, w, f"ragged n={n}")
