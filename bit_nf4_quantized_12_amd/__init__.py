@@ -11,6 +11,8 @@ The function names are those of the C ABI (include/qlora.h):
 * ``qlora_quantize_nf4_dq(w)``
 * ``qlora_dequant(codes, c2, c1, n, dtype)``
 * ``qlora_nf4_matmul(W, act, transposed)``
+* ``qlora_4bit_matmul_lora(W, act, L, R, transposed)``: the same product with a
+  rank term L R^T fused into its epilogue (the kernel the linear layer runs)
 * ``qlora_linear_workspace_bytes(M, N, K, r)``
 * ``qlora_linear_fwd(W, X, A, B, scale, ...)``
 * ``qlora_linear_bwd(W, X, A, B, dY, T, scale, ...)``
@@ -113,6 +115,7 @@ def load_library(path=LIB_PATH):
             "qlora_quantize_4bit": ([vp, i64, i32, i32, vp, vp, vp, vp], i32),
             "qlora_dequant_4bit": ([vp, vp, vp, i64, i32, i32, i32, vp, vp], i32),
             "qlora_4bit_matmul": ([ctypes.POINTER(_Weight4bit), vp, i64, i32, vp, vp], i32),
+            "qlora_4bit_matmul_lora": ([ctypes.POINTER(_Weight4bit), vp, i64, i32, vp, vp, i64, vp, vp], i32),
             "qlora_linear_fwd_4bit": ([ctypes.POINTER(_Weight4bit), vp, vp, vp, i64, i64, f32, vp, vp, vp, sz, vp], i32),
             "qlora_linear_bwd_4bit": ([ctypes.POINTER(_Weight4bit), vp, vp, vp, vp, vp, i64, i64, f32, vp, vp, vp, vp, sz, vp], i32),
         }
@@ -326,6 +329,28 @@ def qlora_nf4_matmul(W, act, transposed=False, out=None):
 qlora_4bit_matmul = qlora_nf4_matmul  # one wrapper serves every stored format
 
 
+def qlora_4bit_matmul_lora(W, act, L, R, transposed=False, out=None):
+    """Base product with a rank term in its epilogue: act W~^T + L R^T ([M, N]) or,
+    transposed, act W~ + L R^T ([M, K]); L [M, rp] and R [Nout, rp] bf16, rp % 64 == 0."""
+    _need(act, torch.bfloat16, "act")
+    _need(L, torch.bfloat16, "L")
+    _need(R, torch.bfloat16, "R")
+    M = act.shape[0]
+    nout = W.cols if transposed else W.rows
+    if act.shape[1] != (W.rows if transposed else W.cols):
+        raise ValueError("act has the wrong number of columns")
+    rp = L.shape[1]
+    if L.shape[0] != M or tuple(R.shape) != (nout, rp):
+        raise ValueError(f"L must be [M, rp] and R [{nout}, rp]")
+    _same_device(act.device, L=L, R=R)
+    _check_weight(W, act.device)
+    out = _buf(out, (M, nout), torch.bfloat16, act.device, "out")
+    w = _weight4_struct(W)
+    _check(load_library().qlora_4bit_matmul_lora(ctypes.byref(w), _ptr(act), M, 1 if transposed else 0, _ptr(L),
+                                                 _ptr(R), rp, _ptr(out), _stream(act.device)))
+    return out
+
+
 def qlora_linear_workspace_bytes(M, N, K, r):
     return int(load_library().qlora_linear_workspace_bytes(M, N, K, r))
 
@@ -351,10 +376,15 @@ def _weight_struct(W):
                        _codebook_id(W.codebook), 1 if W.double_quant else 0), "_4bit"
 
 
+def new_workspace(nbytes, device):
+    """A workspace of nbytes (at least 256) for the linear entry points."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
 def _workspace(M, N, K, r, device, workspace):
     need = qlora_linear_workspace_bytes(M, N, K, r)
     if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        workspace = new_workspace(need, device)
     return workspace
 
 
@@ -413,8 +443,10 @@ class LoRALinear4bitFunction(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, X, A, B, W, scale):
-        Y, T = qlora_linear_fwd(W, X.contiguous(), A.contiguous(), B.contiguous(), scale)
-        ctx.save_for_backward(X, A, B, T)
+        # the kernels need contiguous operands; the backward gets the same copies
+        Xc, Ac, Bc = X.contiguous(), A.contiguous(), B.contiguous()
+        Y, T = qlora_linear_fwd(W, Xc, Ac, Bc, scale)
+        ctx.save_for_backward(Xc, Ac, Bc, T)
         ctx.W = W
         ctx.scale = scale
         return Y
@@ -491,8 +523,7 @@ def qlora_linear_fwd_grouped(W, groups, X, A, B, scale, save_T=True, Y=None, T=N
     Y = _buf(Y, (M, W.rows), torch.bfloat16, dev, "Y")
     T = _buf(T, (M, g * r), torch.float32, dev, "T") if save_T else None
     need = qlora_linear_grouped_workspace_bytes(M, W.rows, K, r, g)
-    ws = workspace if workspace is not None and workspace.numel() >= need else \
-        torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    ws = workspace if workspace is not None and workspace.numel() >= need else new_workspace(need, dev)
     w = _weight4_struct(W)
     _check(load_library().qlora_linear_fwd_grouped(ctypes.byref(w), g, _ptr(X), _ptr(A), _ptr(B), M, r,
                                                    float(scale), _ptr(Y), _ptr(T), _ptr(ws), ws.numel(),
@@ -522,8 +553,7 @@ def qlora_linear_bwd_grouped(W, groups, X, A, B, dY, T, scale, need_dX=True, dX=
     dA = _buf(dA, (g * r, K), torch.bfloat16, dev, "dA")
     dB = _buf(dB, (N, r), torch.bfloat16, dev, "dB")
     need = qlora_linear_grouped_workspace_bytes(M, N, K, r, g)
-    ws = workspace if workspace is not None and workspace.numel() >= need else \
-        torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    ws = workspace if workspace is not None and workspace.numel() >= need else new_workspace(need, dev)
     w = _weight4_struct(W)
     _check(load_library().qlora_linear_bwd_grouped(ctypes.byref(w), g, _ptr(X), _ptr(A), _ptr(B), _ptr(dY),
                                                    _ptr(T), M, r, float(scale), _ptr(dX), _ptr(dA), _ptr(dB),

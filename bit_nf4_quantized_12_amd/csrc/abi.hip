@@ -20,11 +20,13 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int clampi(int64_t v, int64_t lo, int64_t hi) { return (int)(v < lo ? lo : (v > hi ? hi : v)); }
 // Every [rows, cols] operand of the linear layer is indexed in 32 bits:
-// 64 ceil(M / 64) rows (the padded planes) times max(N, K, 64 ceil(r / 64))
-// elements must stay below 2^31 (so byte offsets stay below 2^32).
+// max(64 ceil(M / 64), rp) rows times max(N, K, rp) elements, with
+// rp = 64 ceil(r / 64), must stay below 2^31 (so byte offsets stay below
+// 2^32). The rank side counts as rows too: B^T [r, N], A^T [K, rp] and the
+// gradient partials [rp, N] / [rp, K] are indexed like the token-side planes.
 inline bool index_fits(int64_t M, int64_t N, int64_t K, int64_t r) {
   const int64_t Mp = cdiv(M, 64) * 64, rp = cdiv(r, 64) * 64;
-  return Mp * std::max(std::max(N, K), rp) < (int64_t(1) << 31);
+  return std::max(Mp, rp) * std::max(std::max(N, K), rp) < (int64_t(1) << 31);
 }
 
 // Reduction splits. Each aims at a few hundred workgroups on 256 CUs.
@@ -62,11 +64,10 @@ struct Layout {
 Layout plan(int64_t M, int64_t N, int64_t K, int64_t r, int64_t groups = 1) {
   Layout L;
   const int64_t rp = cdiv(r, 64) * 64;
-  // forward
-  int kslice = 0;
-  L.tsplit = M <= kGemvMaxM ? proj_small_splits((int)K, &kslice) : proj_splits(M, K);
+  // forward (few tokens: T32 holds T [M, r] as the few-token kernel writes it)
+  L.tsplit = M <= kGemvMaxM ? 1 : proj_splits(M, K);
   size_t o = 0;
-  L.partT = o; o = al256(o + (size_t)L.tsplit * M * rp * 4);
+  L.partT = o; o = al256(o + (M <= kGemvMaxM ? 0 : (size_t)L.tsplit * M * rp * 4));
   L.T32 = o;   o = al256(o + (size_t)M * r * 4);
   L.Ts = o;    o = al256(o + (size_t)M * rp * 2);
   L.Bpad = o;  o = al256(o + (rp != r ? (size_t)N * rp * 2 : 0));
@@ -185,22 +186,39 @@ bool device_address(const void* p, void** out) {
     if ((expr) != hipSuccess) return QLORA_ERR_DEVICE; \
   } while (0)
 
-// T = X A^T as split partials [tsplit][M][rp] (tsplit from plan()); A [r, K]
-// (the stacked A of grouped linears: r = g r_seg). Few tokens
-// take the all-loads-in-flight kernel; it is also the one the backward's
-// recompute uses, so a saved and a recomputed T are bit-identical.
-hipError_t project_T(const uint16_t* X, const uint16_t* A, int64_t M, int64_t K, int64_t r, int rp, int tsplit,
-                     float* partT, hipStream_t s) {
-  if (M <= kGemvMaxM) return launch_proj_small(X, A, (int)M, (int)K, (int)r, rp, partT, s);
-  return launch_proj(X, A, (int)M, (int)K, (int)r, rp, tsplit, partT, s);
+// T (float32 [M, r]) recomputed for the backward: few tokens run the few-token
+// kernel's T producers alone (so a saved and a recomputed T are bit-identical),
+// more tokens the streamed projection and its reduction. A [r, K] (the stacked
+// A of grouped linears: r = g r_seg).
+hipError_t recompute_T(const WView& W, const Layout& L, char* base, const uint16_t* X, const uint16_t* A,
+                       int64_t M, int64_t K, int64_t r, hipStream_t s, float** T) {
+  float* T32 = reinterpret_cast<float*>(base + L.T32);
+  *T = T32;
+  if (M <= kGemvMaxM)
+    return launch_fewtok(X, W.codes, W.c2, W.c1, W.absmax, W.cb, (int)W.N, (int)K, (int)M, A, (int)r, nullptr,
+                         (int)r, 0, 0.0f, nullptr, T32, s);
+  const int rp = (int)(cdiv(r, 64) * 64);
+  float* partT = reinterpret_cast<float*>(base + L.partT);
+  uint16_t* Ts = reinterpret_cast<uint16_t*>(base + L.Ts);
+  hipError_t e = launch_proj(X, A, (int)M, (int)K, (int)r, rp, L.tsplit, partT, s);
+  if (e != hipSuccess) return e;
+  return launch_finalize(partT, L.tsplit, (int)M, (int)M, (int)r, rp, 1.0f, T32, Ts, nullptr, s);
 }
 
-int matmul_impl(const WView& W, const void* act, int64_t M, int transposed, void* out, void* stream) {
+// out = act op(W~) (+ L R^T when L is given: L [M, rp], R [Nout, rp]).
+int matmul_impl(const WView& W, const void* act, int64_t M, int transposed, void* out, void* stream,
+                const void* lora_l = nullptr, const void* lora_r = nullptr, int64_t rp = 0) {
   if (!act || !out) return QLORA_ERR_NULL;
   const int64_t N = W.N, K = W.K;
   if (M < 1 || N < 1 || K < 64 || (K % 64) != 0) return QLORA_ERR_SHAPE;
   if (transposed != 0 && transposed != 1) return QLORA_ERR_UNSUPPORTED;
   if (M * std::max(N, K) >= (int64_t(1) << 31) || N * K >= (int64_t(1) << 40)) return QLORA_ERR_SHAPE;
+  if (lora_l) {
+    const int64_t nout = transposed ? K : N;
+    if (rp < 64 || rp > 4096 || rp % 64 != 0 || std::max(M, nout) * rp >= (int64_t(1) << 31))
+      return QLORA_ERR_SHAPE;
+    if (!aligned(lora_l, 16) || !aligned(lora_r, 16)) return QLORA_ERR_ALIGN;
+  }
   if (!aligned(act, 16) || !aligned(out, 16)) return QLORA_ERR_ALIGN;
   try {
     if (tables_status() != 0) return QLORA_ERR_UNSUPPORTED;
@@ -212,10 +230,10 @@ int matmul_impl(const WView& W, const void* act, int64_t M, int transposed, void
     p.absmax = W.absmax;
     p.wN = N;
     p.wK = K;
-    p.lora_l = nullptr;
-    p.lora_r = nullptr;
-    p.rp = 0;
-    p.lora_ld = 0;
+    p.lora_l = static_cast<const uint16_t*>(lora_l);
+    p.lora_r = static_cast<const uint16_t*>(lora_r);
+    p.rp = lora_l ? (int)rp : 0;
+    p.lora_ld = lora_l ? (int)rp : 0;
     p.lora_seg = 0;
     p.out = static_cast<uint16_t*>(out);
     p.M = (int)M;
@@ -250,15 +268,15 @@ int fwd_impl(const WView& W, const void* X, const void* A, const void* B, int64_
     const uint16_t* Ah = static_cast<const uint16_t*>(A);
     const uint16_t* Bh = static_cast<const uint16_t*>(B);
 
-    // T = X A^T: split-K partials [tsplit][M][rp]
-    QLORA_TRY(project_T(Xh, Ah, M, K, r, rp, L.tsplit, partT, s));
     if (M <= kGemvMaxM) {
-      // few tokens: one weight-streaming kernel, which also sums the T
-      // partials, adds the LoRA term and writes T_save
-      QLORA_TRY(launch_gemv(Xh, W.codes, W.c2, W.c1, W.absmax, W.cb, (int)N, (int)K, (int)M, partT, L.tsplit,
-                            rp, Bh, (int)r, scale, static_cast<uint16_t*>(Y), T_save, s));
+      // few tokens: T (into T_save, else the workspace), then one launch
+      // streams the weight and adds the LoRA term
+      QLORA_TRY(launch_fewtok(Xh, W.codes, W.c2, W.c1, W.absmax, W.cb, (int)N, (int)K, (int)M, Ah, (int)r, Bh,
+                              (int)r, 0, scale, static_cast<uint16_t*>(Y), T32, s));
       return QLORA_OK;
     }
+    // T = X A^T: split-K partials [tsplit][M][rp]
+    QLORA_TRY(launch_proj(Xh, Ah, (int)M, (int)K, (int)r, rp, L.tsplit, partT, s));
     // Ts = bf16(scale * T) [M, rp], T float32 [M, r]
     QLORA_TRY(launch_finalize(partT, L.tsplit, (int)M, (int)M, (int)r, rp, scale, T32, Ts, nullptr, s));
     const uint16_t* Br = Bh;
@@ -334,11 +352,8 @@ int bwd_impl(const WView& W, const void* X, const void* A, const void* B, const 
     // T (float32 [M, r]): saved by the forward, or recomputed
     const float* T = T_saved;
     if (!T) {
-      float* partT = reinterpret_cast<float*>(base + L.partT);
-      float* T32 = reinterpret_cast<float*>(base + L.T32);
-      uint16_t* Ts = reinterpret_cast<uint16_t*>(base + L.Ts);
-      QLORA_TRY(project_T(Xh, Ah, M, K, r, rp, L.tsplit, partT, s));
-      QLORA_TRY(launch_finalize(partT, L.tsplit, (int)M, (int)M, (int)r, rp, 1.0f, T32, Ts, nullptr, s));
+      float* T32 = nullptr;
+      QLORA_TRY(recompute_T(W, L, base, Xh, Ah, M, K, r, s, &T32));
       T = T32;
     }
     // U = dY B: B^T [r, N] is the row operand of the projection; A^T [K, rp]
@@ -429,13 +444,13 @@ int fwd_grouped_impl(const WView& W, int64_t g, const void* X, const void* A, co
     const uint16_t* Xh = static_cast<const uint16_t*>(X);
     const uint16_t* Ah = static_cast<const uint16_t*>(A);
     const uint16_t* Bh = static_cast<const uint16_t*>(B);
-    // T = X [A_1; ..; A_g]^T: one pass over X for all segments
-    QLORA_TRY(project_T(Xh, Ah, M, K, R, (int)R, L.tsplit, partT, s));
     if (M <= kGemvMaxM) {
-      QLORA_TRY(launch_gemv(Xh, W.codes, W.c2, W.c1, W.absmax, W.cb, (int)N, (int)K, (int)M, partT, L.tsplit,
-                            (int)R, Bh, (int)r, scale, static_cast<uint16_t*>(Y), T_save, s, (int)Ns, (int)R));
+      QLORA_TRY(launch_fewtok(Xh, W.codes, W.c2, W.c1, W.absmax, W.cb, (int)N, (int)K, (int)M, Ah, (int)R, Bh,
+                              (int)r, (int)Ns, scale, static_cast<uint16_t*>(Y), T32, s));
       return QLORA_OK;
     }
+    // T = X [A_1; ..; A_g]^T: one pass over X for all segments
+    QLORA_TRY(launch_proj(Xh, Ah, (int)M, (int)K, (int)R, (int)R, L.tsplit, partT, s));
     QLORA_TRY(launch_finalize(partT, L.tsplit, (int)M, (int)M, (int)R, (int)R, scale, T32, Ts, nullptr, s));
     GemmParams p;
     p.act = Xh;
@@ -502,11 +517,8 @@ int bwd_grouped_impl(const WView& W, int64_t g, const void* X, const void* A, co
     float* gpartB = reinterpret_cast<float*>(base + L.gpartB);
     const float* T = T_saved;
     if (!T) {
-      float* partT = reinterpret_cast<float*>(base + L.partT);
-      float* T32 = reinterpret_cast<float*>(base + L.T32);
-      uint16_t* Ts = reinterpret_cast<uint16_t*>(base + L.Ts);
-      QLORA_TRY(project_T(Xh, Ah, M, K, R, (int)R, L.tsplit, partT, s));
-      QLORA_TRY(launch_finalize(partT, L.tsplit, (int)M, (int)M, (int)R, (int)R, 1.0f, T32, Ts, nullptr, s));
+      float* T32 = nullptr;
+      QLORA_TRY(recompute_T(W, L, base, Xh, Ah, M, K, R, s, &T32));
       T = T32;
     }
     // B^T [r, N] (segment i in columns i Ns ..) and [A_1; ..; A_g]^T [K, R]
@@ -688,6 +700,15 @@ int qlora_4bit_matmul(const qlora_4bit_weight* W, const void* act, int64_t M, in
   WView v;
   const int st = view_4bit(W, v);
   return st != QLORA_OK ? st : matmul_impl(v, act, M, transposed, out, stream);
+}
+
+int qlora_4bit_matmul_lora(const qlora_4bit_weight* W, const void* act, int64_t M, int transposed,
+                           const void* L, const void* R, int64_t rp, void* out, void* stream) {
+  WView v;
+  const int st = view_4bit(W, v);
+  if (st != QLORA_OK) return st;
+  if (!L || !R) return QLORA_ERR_NULL;
+  return matmul_impl(v, act, M, transposed, out, stream, L, R, rp);
 }
 
 int qlora_adamw_step(float* param_f32, void* param_bf16, const void* grad_bf16, float* m, float* v,

@@ -1,27 +1,33 @@
-// Few-token forward (M <= 16): Y = X W~^T + s T B^T, bound by reading the
-// 4-bit weight from HBM.
+// Few-token forward (M <= 16): Y = X W~^T + s T B^T with T = X A^T, in one
+// launch, bound by reading the 4-bit weight from HBM.
 //
 // "QLoRA: Efficient Finetuning of Quantized LLMs" (inquiringlines.com),
-// "Method": dequantise to BFloat16, multiply in 16-bit. With at most 16
-// tokens each weight is used at most 16 times, so the kernel streams the
-// codes exactly once, straight from HBM into registers:
+// "Method": dequantise to BFloat16, multiply in 16-bit. The LoRA term follows
+// "QLoRA: Efficient Fine-Tuning of Quantized Language Models"
+// (mbrenndoerfer.com), section "Low-Rank Adaptation (LoRA)". With at most 16
+// tokens each weight is used at most 16 times, so the kernel streams the codes
+// exactly once, straight from HBM into registers.
 //
-//  * a workgroup (8 wave64) owns 16 weight rows over the whole of K; the
-//    waves take 128-column chunks round robin, 4 at a time with all four
-//    chunks' loads in flight before any unpacking, and meet in LDS at the
-//    end, so there are no split-K partial sums in memory. Workgroups are
-//    small enough for two per CU, so a 7B projection's codes are almost all
-//    in flight at once;
-//  * per chunk a lane loads 16 B of codes = 32 weights of its row (one
-//    global_load_dwordx4), unpacks them through its block's 16-entry bf16
-//    table with v_perm byte selects, and feeds four
-//    v_mfma_f32_16x16x32_bf16 with X rows as the A operand. X rows past M
-//    are read as zero by a buffer load whose offset lies past the buffer
-//    (no memory traffic); their output rows are never stored. The reduction
-//    order inside a chunk is permuted (MFMA k-slot 8 g + e of product i is
-//    column 32 g + 8 i + e of the chunk), identically for both operands;
-//  * the epilogue sums the split-K partials of T = X A^T (proj_small_kernel
-//    below, a separate launch) and adds s T B^T before the bf16 store.
+// Two launches on the stream: the first computes T (each workgroup a few
+// columns of T = X A^T over the whole reduction, float32, written once; the
+// backward's recompute of T runs the same launch, so a saved and a recomputed
+// T are bit-identical), the second streams the weight and adds s T B^T at its
+// epilogue. (A single launch whose first workgroups published T to the others
+// through a counter measured 2-3x slower: while the weight stream saturates
+// HBM, the release, the atomic and the polls each wait behind that traffic,
+// and the handoff took 5-10 us.)
+//
+//  * stream layout: 8 wave64; lane l has weight row c = l & 15 of the
+//    workgroup and slot s = 4 w + (l >> 4) of 32; slot s takes the 64-weight
+//    blocks s, s + 32, s + 64, .. of its row, one block (32 B of codes, one
+//    constant) per step, the loads of two steps issued together. A block's 16-entry
+//    table of bf16(q[c] c^) turns its 8 code words into 8
+//    v_mfma_f32_16x16x32_bf16 B operands (v_perm byte selects, exact W~); the
+//    A operand is X (token m = l & 15, the same 64 columns; tokens past M read
+//    as zero by out-of-range buffer loads, no memory traffic).
+//  * the 8 waves' partial 16 x 16 tiles meet in LDS; the epilogue adds
+//    s T B^T in float32 (four accumulators per output) before the one bf16
+//    rounding.
 #include "launch.hpp"
 
 namespace qlora {
@@ -31,8 +37,9 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// 16-entry bf16(q[c] * c^) table as byte planes (see the GEMM kernel).
-__device__ __forceinline__ void gv_table(float chat, const Levels& lv, uint32_t L[4], uint32_t H[4]) {
+// 16-entry bf16(q[c] * c^) table as byte planes: L[j] holds the low bytes of
+// entries 4j .. 4j+3, H[j] the high bytes.
+__device__ __forceinline__ void ft_table(float chat, const Levels& lv, uint32_t L[4], uint32_t H[4]) {
   uint32_t P[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) P[i] = pack_bf16(__fmul_rn(lv.q[2 * i], chat), __fmul_rn(lv.q[2 * i + 1], chat));
@@ -43,8 +50,9 @@ __device__ __forceinline__ void gv_table(float chat, const Levels& lv, uint32_t 
   }
 }
 
-// 8 codes -> 8 bf16 of W~ in natural order (4 packed pairs).
-__device__ __forceinline__ uint4 gv_lookup8(uint32_t d, const uint32_t L[4], const uint32_t H[4]) {
+// 8 codes (element i in nibble i) -> 8 bf16 of W~ in natural order. Selector
+// bytes: the low 3 bits pick an entry inside a half table, bit 3 the half.
+__device__ __forceinline__ uint4 ft_lookup8(uint32_t d, const uint32_t L[4], const uint32_t H[4]) {
   const uint32_t se = d & 0x07070707u;
   const uint32_t so = (d >> 4) & 0x07070707u;
   const uint32_t ce = ((d >> 1) & 0x04040404u) | 0x03020100u;
@@ -59,12 +67,11 @@ __device__ __forceinline__ uint4 gv_lookup8(uint32_t d, const uint32_t L[4], con
                     perm(O1, E1, 0x07060302u));
 }
 
-constexpr int GV_WAVES = 8;            // waves per workgroup
-constexpr int GV_D = 4;                // 128-column chunks in flight per wave
-constexpr int GV_NT = 64 * GV_WAVES;
-constexpr int GV_PRE = 4;              // T partials per element fetched before the weight stream
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int FT_WAVES = 8;
+constexpr int FT_NT = 64 * FT_WAVES;
+constexpr int FT_SLOTS = 4 * FT_WAVES;  // 64-column blocks per workgroup step
+constexpr int FT_D = 2;                 // steps whose loads are issued together
+constexpr int FT_RMAX = 256;            // rank columns of one segment
 
 // 16 B of a bf16 matrix through a buffer resource: zero when off is past the
 // resource's size (then nothing is read).
@@ -73,243 +80,292 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t rs, uint32_t 
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// X [M, K] bf16 as a buffer; lane row c >= M reads past the end (zeros).
-struct XRows {
+// Row `row` of a bf16 matrix [rows, K] as a buffer; rows past `rows` read as
+// zero (this lane's offset is then the buffer's end).
+struct RowBuf {
   __amdgpu_buffer_rsrc_t rs;
-  uint32_t row_off, end;  // byte offset of this lane's row, or end when c >= M
-  __device__ XRows(const uint16_t* X, int M, int K, int c) {
-    end = (uint32_t)M * (uint32_t)K * 2u;  // < 2^32: M max(N, K) < 2^31
-    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), 0, (int)end, 0x00020000);
-    row_off = c < M ? (uint32_t)c * (uint32_t)K * 2u : end;
+  uint32_t base, end;
+  __device__ RowBuf(const uint16_t* p, int rows, int K, int row) {
+    end = (uint32_t)rows * (uint32_t)K * 2u;  // < 2^32 (checked on the host)
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), 0, (int)end, 0x00020000);
+    base = row < rows ? (uint32_t)row * (uint32_t)K * 2u : end;
   }
-  // 4 x 8 bf16 at columns k, k + 8, k + 16, k + 24 of this lane's row
-  __device__ __forceinline__ void load4(int k, uint4 (&v)[4]) const {
-    const uint32_t o = row_off == end ? end : row_off + 2u * (uint32_t)k;
+  // the 64 bf16 of block b (columns 64 b ..) of this lane's row
+  __device__ __forceinline__ void load_block(int b, uint4 (&v)[8]) const {
+    const uint32_t o = base == end ? end : base + 128u * (uint32_t)b;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = buf_load16(rs, o == end ? end : o + 16u * i);
+    for (int i = 0; i < 8; ++i) v[i] = buf_load16(rs, o == end ? end : o + 16u * i);
   }
 };
 
+}  // namespace
+
+struct FewTokParams {
+  const uint16_t* X;     // [M, K]
+  const uint8_t* codes;  // weight [N, K]
+  const uint8_t* c2;
+  const float* c1;
+  const float* absmax;   // fp32 block constants (no double quantisation), or null
+  const uint16_t* A;     // [R, K] (the segments' A stacked)
+  const uint16_t* B;     // [N, rseg]
+  uint16_t* Y;           // [M, N]
+  float* T;              // [M, R] float32: written by the producers
+  int M, N, K, R, rseg, segN;  // segN: rows per segment (grouped), 0 = one segment
+  int P, J;              // T workgroups, T columns each (T launch)
+  float scale;
+  Levels lv;
+};
+
+namespace {
+
+// Producer: T[m][j] = sum_k X[m][k] A[j][k] for j in [j0, j0 + J) (J <= 16),
+// m < M. Per column j and group of up to 8 tokens, thread t takes the
+// 8-column chunks t, t + FT_NT, .. (the A chunk and the tokens' X chunks in
+// flight together), multiplies in float32 (bf16 products are exact), and the
+// FT_NT partial sums of each (m, j) are added by a fixed-order tree in LDS.
+// The T-only launch of the backward runs this same code.
+constexpr int FT_PM = 8;  // tokens per pass
+__device__ void ft_produce(const FewTokParams& p, int j0, float* red) {
+  const int tid = threadIdx.x;
+  const int nch = p.K >> 3;
+  const int nj = min(p.J, p.R - j0);
+  for (int jj = 0; jj < nj; ++jj) {
+    const uint16_t* arow = p.A + (int64_t)(j0 + jj) * p.K;
+    for (int m0 = 0; m0 < p.M; m0 += FT_PM) {
+      float acc[FT_PM];
+#pragma unroll
+      for (int i = 0; i < FT_PM; ++i) acc[i] = 0.0f;
+      for (int ch = tid; ch < nch; ch += FT_NT) {
+        const uint4 av = *reinterpret_cast<const uint4*>(arow + 8 * ch);
+        uint4 xv[FT_PM];
+#pragma unroll
+        for (int i = 0; i < FT_PM; ++i)
+          xv[i] = *reinterpret_cast<const uint4*>(p.X + (int64_t)min(m0 + i, p.M - 1) * p.K + 8 * ch);
+        const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+        for (int i = 0; i < FT_PM; ++i) {
+          const uint32_t xw[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+          float a = acc[i];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            a = __builtin_fmaf(bf16lo(xw[q]), bf16lo(aw[q]), a);
+            a = __builtin_fmaf(bf16hi(xw[q]), bf16hi(aw[q]), a);
+          }
+          acc[i] = a;
+        }
+      }
+      // fixed-order tree over the FT_NT threads
+#pragma unroll
+      for (int i = 0; i < FT_PM; ++i) red[i * FT_NT + tid] = acc[i];
+      __syncthreads();
+      for (int h = FT_NT / 2; h > 0; h >>= 1) {
+        if (tid < h) {
+#pragma unroll
+          for (int i = 0; i < FT_PM; ++i) red[i * FT_NT + tid] += red[i * FT_NT + tid + h];
+        }
+        __syncthreads();
+      }
+      if (tid < FT_PM && m0 + tid < p.M) p.T[(int64_t)(m0 + tid) * p.R + j0 + jj] = red[tid * FT_NT];
+      __syncthreads();
+    }
+  }
+}
+
+// T = X A^T: workgroup w computes columns w J .. w J + J - 1.
+__global__ __launch_bounds__(FT_NT) void fewtok_t_kernel(FewTokParams p) {
+  __shared__ float pred[FT_PM * FT_NT];
+  ft_produce(p, blockIdx.x * p.J, pred);
+}
+
+// Y = X W~^T + scale T_z B^T: workgroup w owns weight rows 16 w .. 16 w + 15.
 template <bool ABS>
-__global__ __launch_bounds__(GV_NT) __attribute__((amdgpu_waves_per_eu(4))) void gemv_kernel(
-    const uint16_t* __restrict__ X, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ c2,
-    const float* __restrict__ c1, const float* __restrict__ absmax, int N, int K, int M,
-    const float* __restrict__ tpart, int tsplit, int rp,
-    const uint16_t* __restrict__ B, int r, float scale, uint16_t* __restrict__ Y, float* __restrict__ T_out,
-    int segN, int tld, Levels lv) {
-  __shared__ float red[GV_WAVES][16][17];
-  __shared__ float sT[16][257];
-  __shared__ uint16_t sB[16 * 256];  // the workgroup's 16 rows of B
+__global__ __launch_bounds__(FT_NT) __attribute__((amdgpu_waves_per_eu(4))) void fewtok_kernel(FewTokParams p) {
+  __shared__ float red[FT_WAVES][16][17];
+  __shared__ float sT[16][FT_RMAX + 4];
+  __shared__ uint16_t sB[16][FT_RMAX + 8];
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n0 = blockIdx.x * 16;
-  // grouped linears: rows of segment z = n0 / segN use T columns z r .. + r
-  // (T_out [M, tld] gets them from the segment's first workgroup)
-  const int zc = segN ? (n0 / segN) * r : 0;
-  const bool t_writer = segN ? (n0 % segN) == 0 : blockIdx.x == 0;
   const int c = l & 15, g = l >> 4;
-  const int n = min(n0 + c, N - 1);  // rows past N: clamped read, result not stored
-  const XRows xr(X, M, K, c);
-  const int64_t rowe = (int64_t)n * K;
-  const int nchunks = (K + 127) / 128;
+  const int slot = 4 * w + g;
+  const int n0 = blockIdx.x * 16;
+  const int n = min(n0 + c, p.N - 1);  // rows past N: clamped read, result not stored
+  const int nbk = p.K >> 6;
+  const int64_t rowb = (int64_t)n * nbk;  // first block of this lane's row
+  const RowBuf xr(p.X, p.M, p.K, c);
+  const int steps = (nbk + FT_SLOTS - 1) / FT_SLOTS;
+  // grouped linears: rows of segment z use T columns z rseg .. + rseg
+  const int zc = p.segN ? (n0 / p.segN) * p.rseg : 0;
 
-  // Epilogue operands first, so that their latency overlaps the weight
-  // stream: thread t owns T elements t and t + GV_NT (< M r) with their first
-  // GV_PRE split partials, and B elements t and t + GV_NT (< 16 r).
-  const int nb = 16 * r, nt = M * r;
-  // Addresses are clamped so that every load is unconditional (one batch,
-  // no waits between them); unused values are masked afterwards.
-  float tp[2][GV_PRE];
-  uint16_t bval[2];
+  // T[m][zc .. zc + rseg) (float32, written by the previous launch on this
+  // stream), zero-padded to a multiple of 4 columns: elements idx = tid and
+  // tid + FT_NT of the [M, rs4] block fetched before the weight stream (all
+  // of it for M rs4 <= 1024), the rest at the epilogue
+  const int rs4 = (p.rseg + 3) & ~3;
+  auto t_elem = [&](int idx) -> float {
+    const int m = idx / rs4, j = idx - m * rs4;
+    return idx < p.M * rs4 && j < p.rseg ? p.T[(int64_t)m * p.R + zc + j] : 0.0f;
+  };
+  const float tv0 = t_elem(tid), tv1 = t_elem(tid + FT_NT);
+
+  // B rows n0 .. n0 + 15 (rseg bf16 each), fetched before the weight stream:
+  // 16-byte pieces when rseg % 8 == 0, else single elements (<= 8 a thread)
+  const bool bvec = (p.rseg & 7) == 0;
+  const int nbv = bvec ? 2 * p.rseg : 16 * p.rseg;
+  uint4 bv = make_uint4(0, 0, 0, 0);
+  uint16_t bs[8];
+  if (bvec) {
+    if (tid < nbv) {
+      const int br = tid / (p.rseg / 8), bc = tid % (p.rseg / 8);
+      bv = *reinterpret_cast<const uint4*>(p.B + (int64_t)min(n0 + br, p.N - 1) * p.rseg + 8 * bc);
+    }
+  } else {
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int idx = tid + e * GV_NT;
-    const bool hb = idx < nb, ht = idx < nt;
-    const int br = hb ? idx / r : 0, bj = hb ? idx % r : 0;
-    bval[e] = B[(int64_t)min(n0 + br, N - 1) * r + bj];  // stored only when hb
-    const int tm = ht ? idx / r : 0, tj = ht ? idx % r : 0;
-#pragma unroll
-    for (int k = 0; k < GV_PRE; ++k) tp[e][k] = tpart[((int64_t)min(k, tsplit - 1) * M + tm) * rp + zc + tj];
+    for (int k = 0; k < 8; ++k) {
+      const int idx = tid + FT_NT * k;
+      const int br = idx / p.rseg, bc = idx - br * p.rseg;
+      bs[k] = idx < nbv ? p.B[(int64_t)min(n0 + br, p.N - 1) * p.rseg + bc] : (uint16_t)0;
+    }
   }
 
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int cb = w; cb < nchunks; cb += GV_D * GV_WAVES) {
-    // this lane's 32 columns of each chunk; K % 64 == 0, so only the upper
-    // half of the last chunk can be missing (clamped read, c^ = 0)
-    uint4 cw[GV_D];
-    float craw[GV_D], g1[GV_D];
-    uint32_t c2b[GV_D];
-    int kc[GV_D];
-#pragma unroll
-    for (int i = 0; i < GV_D; ++i) {
-      const int ch = min(cb + i * GV_WAVES, nchunks - 1);  // past the end: a repeat, masked below
-      kc[i] = min(128 * ch + 32 * g, K - 32);
-      const int64_t e = rowe + kc[i];
-      cw[i] = *reinterpret_cast<const uint4*>(codes + (e >> 1));
-      if (ABS) {
-        craw[i] = absmax[e >> 6];
-      } else {
-        c2b[i] = c2[e >> 6];
-        g1[i] = c1[e >> 14];
-      }
+  // Loads of step i: the lane's 32 B of codes, its block constant, and the
+  // 64 X values of token c at the block's columns. Addresses are clamped so
+  // that every load is unconditional; a step past the row's end is masked.
+  struct Step {
+    uint4 cw0, cw1;
+    uint4 xv[8];
+    float craw;
+    uint32_t c2b;
+    float g1;
+  };
+  auto issue = [&](int i, Step& st) {
+    const int b = min(slot + FT_SLOTS * i, nbk - 1);
+    const int64_t e = rowb + b;  // block index
+    const uint4* cp = reinterpret_cast<const uint4*>(p.codes + 32 * e);
+    st.cw0 = cp[0];
+    st.cw1 = cp[1];
+    if (ABS) {
+      st.craw = p.absmax[e];
+    } else {
+      st.c2b = p.c2[e];
+      st.g1 = p.c1[e >> 8];
     }
-    uint4 xv[GV_D][4];
+    xr.load_block(b, st.xv);
+  };
+
+  // Batches of FT_D steps: a batch's loads are all issued, then consumed in
+  // order (no load is outstanding across the loop edge, so every wait is a
+  // counted one). A step past the row's end reloads a valid block and is
+  // masked: c^ = 0 and X = 0 add exact zeros.
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < steps; i += FT_D) {
+    Step st[FT_D];
+    // scheduling barriers keep the issue order (step 0's loads before step
+    // 1's) and the compute order, so step d waits only for its own loads
 #pragma unroll
-    for (int i = 0; i < GV_D; ++i) xr.load4(kc[i], xv[i]);
-    // Every chunk slot is multiplied (no branch, so the compiler keeps all
-    // loads ahead of the first product); a slot past the end, or the missing
-    // upper half of a last chunk, has c^ = 0 and X = 0 and adds exact zeros.
+    for (int d = 0; d < FT_D; ++d) {
+      issue(i + d, st[d]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
-    for (int i = 0; i < GV_D; ++i) {
-      const bool ok = 128 * (cb + i * GV_WAVES) + 32 * g < K;
-      const float cf = ABS ? craw[i] : __fmul_rn(e4m3_value(c2b[i]), g1[i]);
+    for (int d = 0; d < FT_D; ++d) {
+      if (d) __builtin_amdgcn_sched_barrier(0);
+      const bool ok = slot + FT_SLOTS * (i + d) < nbk;
+      const float cf = ABS ? st[d].craw : __fmul_rn(e4m3_value(st[d].c2b), st[d].g1);
       uint32_t L[4], H[4];
-      gv_table(ok ? cf : 0.0f, lv, L, H);
-      const uint32_t words[4] = {cw[i].x, cw[i].y, cw[i].z, cw[i].w};
+      ft_table(ok ? cf : 0.0f, p.lv, L, H);
+      const uint32_t words[8] = {st[d].cw0.x, st[d].cw0.y, st[d].cw0.z, st[d].cw0.w,
+                                 st[d].cw1.x, st[d].cw1.y, st[d].cw1.z, st[d].cw1.w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint4 wv = gv_lookup8(words[q], L, H);
-        const uint4 x = ok ? xv[i][q] : make_uint4(0, 0, 0, 0);
+      for (int t = 0; t < 8; ++t) {
+        const uint4 wv = ft_lookup8(words[t], L, H);
+        const uint4 x = ok ? st[d].xv[t] : make_uint4(0, 0, 0, 0);
         acc = mfma16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, wv), acc);
       }
     }
   }
-  // D[m][n]: lane holds X rows 4 g + v, weight row c
+  // D[m][row]: lane holds tokens 4 g + v, weight row c
 #pragma unroll
   for (int v = 0; v < 4; ++v) red[w][4 * g + v][c] = acc[v];
-
-  // B rows n0 .. n0 + 15 (r columns each) and T = sum of the split-K
-  // partials of X A^T (rows < M, columns < r) into LDS; partials are added
-  // in split order from 0
+  if (bvec) {
+    if (tid < nbv) {
+      const int br = tid / (p.rseg / 8), bc = tid % (p.rseg / 8);
+      *reinterpret_cast<uint4*>(&sB[br][8 * bc]) = bv;
+    }
+  } else {
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    // keeps the compiler from consuming (and waiting for) the early loads
-    // before the weight stream
-#pragma unroll
-    for (int k = 0; k < GV_PRE; ++k) asm volatile("" : "+v"(tp[e][k]));
-    const int idx = tid + e * GV_NT;
-    if (idx < nb) sB[idx] = bval[e];
-    if (idx < nt) {
-      const int tm = idx / r, tj = idx % r;
-      float s = 0.0f;
-#pragma unroll
-      for (int k = 0; k < GV_PRE; ++k) s += k < tsplit ? tp[e][k] : 0.0f;
-      for (int k = GV_PRE; k < tsplit; ++k) s += tpart[((int64_t)k * M + tm) * rp + zc + tj];
-      sT[tm][tj] = s;
-      if (t_writer && T_out) T_out[(int64_t)tm * tld + zc + tj] = s;
+    for (int k = 0; k < 8; ++k) {
+      const int idx = tid + FT_NT * k;
+      const int br = idx / p.rseg, bc = idx - br * p.rseg;
+      if (idx < nbv) sB[br][bc] = bs[k];
     }
   }
-  // r > 64: the rest of B and T
-  for (int idx = tid + 2 * GV_NT; idx < nb; idx += GV_NT) {
-    const int rr = idx / r, j = idx % r;
-    sB[idx] = B[(int64_t)min(n0 + rr, N - 1) * r + j];
+
+  for (int idx = tid; idx < p.M * rs4; idx += FT_NT) {
+    const float v = idx == tid ? tv0 : idx == tid + FT_NT ? tv1 : t_elem(idx);
+    sT[idx / rs4][idx % rs4] = v;
   }
-  for (int idx = tid + 2 * GV_NT; idx < nt; idx += GV_NT) {
-    const int m = idx / r, j = idx % r;
-    float s = 0.0f;
-    for (int k = 0; k < tsplit; ++k) s += tpart[((int64_t)k * M + m) * rp + zc + j];
-    sT[m][j] = s;
-    if (t_writer && T_out) T_out[(int64_t)m * tld + zc + j] = s;
-  }
+  if (tid < 16 * 4) sB[tid >> 2][p.rseg + (tid & 3)] = 0;
   __syncthreads();
-  // thread -> (m, row): m = tid >> 4, row = tid & 15 (first 256 threads)
-  const int m = tid >> 4, rr = tid & 15;
-  if (tid < 256 && m < M && n0 + rr < N) {
+  // outputs (m, row): y = sum of the waves' tiles + s sum_j T[m][j] B[row][j]
+  if (tid < 16 * p.M) {
+    const int m = tid >> 4, rr = tid & 15;
     float y = 0.0f;
 #pragma unroll
-    for (int q = 0; q < GV_WAVES; ++q) y += red[q][m][rr];
-    float lo = 0.0f;
-    for (int j = 0; j < r; ++j) lo = __builtin_fmaf(sT[m][j], bf16lo(sB[rr * r + j]), lo);
-    const __bf16 h = (__bf16)(y + scale * lo);
-    Y[(int64_t)m * N + n0 + rr] = __builtin_bit_cast(uint16_t, h);
-  }
-}
-
-// T partials for few tokens (M <= 16): part[ks][m][j] = sum over reduction
-// slice ks (kslice columns, a multiple of 128) of X[m][k] R[j][k], for
-// j < rows. R is the rank-side factor (A, or [A_1; ..; A_g]); a workgroup
-// (4 wave64) owns 16 of its rows, and its waves take 128-column chunks round
-// robin, two at a time with all loads in flight, like gemv_kernel with
-// plain bf16 in place of the 4-bit codes.
-constexpr int PS_WAVES = 4;
-__global__ __launch_bounds__(64 * PS_WAVES) void proj_small_kernel(const uint16_t* __restrict__ X,
-                                                                    const uint16_t* __restrict__ R, int M, int K,
-                                                                    int rows, int rp, int kslice,
-                                                                    float* __restrict__ part) {
-  __shared__ float red[PS_WAVES][16][17];
-  const int tid = threadIdx.x, l = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int j0 = blockIdx.x * 16, ks = blockIdx.y;
-  const int c = l & 15, g = l >> 4;
-  const XRows xr(X, M, K, c);
-  const uint16_t* rrow = R + (int64_t)min(j0 + c, rows - 1) * K;  // rows past the end: clamped, not stored
-  const int kb = ks * kslice, ke = min(K, kb + kslice);
-  const int nch = (ke - kb + 127) / 128;
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int cb = w; cb < nch; cb += 2 * PS_WAVES) {
-    uint4 av[2][4], xv[2][4];
-    bool ok[2];
+    for (int q = 0; q < FT_WAVES; ++q) y += red[q][m][rr];
+    // columns rseg .. rseg+3 of sT / sB are zero
+    float lo[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < p.rseg; j += 4) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ch = cb + i * PS_WAVES;  // wave-uniform
-      const int k = kb + 128 * ch + 32 * g;
-      ok[i] = ch < nch && k < ke;      // only the upper half of the last chunk can be missing
-      const int kk = ok[i] ? k : kb;   // else a repeat of valid columns, masked below
-#pragma unroll
-      for (int q = 0; q < 4; ++q) av[i][q] = *reinterpret_cast<const uint4*>(rrow + kk + 8 * q);
-      xr.load4(kk, xv[i]);
+      for (int e = 0; e < 4; ++e) lo[e] = __builtin_fmaf(sT[m][j + e], bf16lo(sB[rr][j + e]), lo[e]);
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {  // a masked slot adds exact zeros
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint4 a = ok[i] ? av[i][q] : make_uint4(0, 0, 0, 0);
-        acc = mfma16(__builtin_bit_cast(bf16x8, xv[i][q]), __builtin_bit_cast(bf16x8, a), acc);
-      }
-    }
-  }
-#pragma unroll
-  for (int v = 0; v < 4; ++v) red[w][4 * g + v][c] = acc[v];
-  __syncthreads();
-  const int m = tid >> 4, jj = tid & 15;
-  if (m < M && j0 + jj < rows) {
-    float t = 0.0f;
-#pragma unroll
-    for (int q = 0; q < PS_WAVES; ++q) t += red[q][m][jj];
-    part[((int64_t)ks * M + m) * rp + j0 + jj] = t;
+    const float lsum = (lo[0] + lo[1]) + (lo[2] + lo[3]);
+    const float out = y + p.scale * lsum;
+    if (n0 + rr < p.N) p.Y[(int64_t)m * p.N + n0 + rr] = __builtin_bit_cast(uint16_t, (__bf16)out);
   }
 }
 
 }  // namespace
 
-hipError_t launch_gemv(const uint16_t* X, const uint8_t* codes, const uint8_t* c2, const float* c1,
-                       const float* absmax, int codebook, int N, int K, int M, const float* tpart, int tsplit,
-                       int rp, const uint16_t* B, int r, float scale, uint16_t* Y, float* T_out, hipStream_t s,
-                       int segN, int tld) {
-  if (!tld) tld = r;
+// T launch: J = ceil(R / 256) T columns per workgroup (at most 16, so R <=
+// 4096), P = ceil(R / J) workgroups.
+static void ft_producers(int R, int* P, int* J) {
+  int j = (R + 255) / 256;
+  if (j < 1) j = 1;
+  *J = j;
+  *P = (R + j - 1) / j;
+}
+
+hipError_t launch_fewtok(const uint16_t* X, const uint8_t* codes, const uint8_t* c2, const float* c1,
+                         const float* absmax, int codebook, int N, int K, int M, const uint16_t* A, int R,
+                         const uint16_t* B, int rseg, int segN, float scale, uint16_t* Y, float* T,
+                         hipStream_t s) {
+  FewTokParams p;
+  p.X = X;
+  p.codes = codes;
+  p.c2 = c2;
+  p.c1 = c1;
+  p.absmax = absmax;
+  p.A = A;
+  p.B = B;
+  p.Y = Y;
+  p.T = T;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.R = R;
+  p.rseg = rseg;
+  p.segN = segN;
+  ft_producers(R, &p.P, &p.J);
+  p.scale = scale;
+  p.lv = host_levels(codebook);
+  hipLaunchKernelGGL(fewtok_t_kernel, dim3(p.P), dim3(FT_NT), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !Y) return e;
+  const dim3 grid((N + 15) / 16);
   if (absmax)
-    hipLaunchKernelGGL(gemv_kernel<true>, dim3((N + 15) / 16), dim3(GV_NT), 0, s, X, codes, c2, c1, absmax, N, K,
-                       M, tpart, tsplit, rp, B, r, scale, Y, T_out, segN, tld, host_levels(codebook));
+    hipLaunchKernelGGL(fewtok_kernel<true>, grid, dim3(FT_NT), 0, s, p);
   else
-    hipLaunchKernelGGL(gemv_kernel<false>, dim3((N + 15) / 16), dim3(GV_NT), 0, s, X, codes, c2, c1, absmax, N, K,
-                       M, tpart, tsplit, rp, B, r, scale, Y, T_out, segN, tld, host_levels(codebook));
-  return hipGetLastError();
-}
-
-int proj_small_splits(int K, int* kslice) {
-  int ts = (K + 1023) / 1024;
-  if (ts > GV_PRE) ts = GV_PRE;
-  const int ks = ((K + ts - 1) / ts + 127) / 128 * 128;
-  *kslice = ks;
-  return (K + ks - 1) / ks;
-}
-
-hipError_t launch_proj_small(const uint16_t* X, const uint16_t* R, int M, int K, int rows, int rp, float* part,
-                             hipStream_t s) {
-  int kslice = 0;
-  const int ts = proj_small_splits(K, &kslice);
-  hipLaunchKernelGGL(proj_small_kernel, dim3((rows + 15) / 16, ts), dim3(64 * PS_WAVES), 0, s, X, R, M, K, rows, rp,
-                     kslice, part);
+    hipLaunchKernelGGL(fewtok_kernel<false>, grid, dim3(FT_NT), 0, s, p);
   return hipGetLastError();
 }
 

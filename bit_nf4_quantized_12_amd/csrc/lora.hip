@@ -566,16 +566,16 @@ __global__ __launch_bounds__(256) void transpose2_kernel(const uint16_t* __restr
                                                           int K, int r, int rA, int rp,
                                                           uint16_t* __restrict__ Bt,
                                                           uint16_t* __restrict__ At) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  const int nb = r * N;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nb = (int64_t)r * N;
   if (idx < nb) {
-    const int j = idx / N, n = idx - j * N;
+    const int64_t j = idx / N, n = idx - j * N;
     Bt[idx] = B[n * r + j];
     return;
   }
-  const int ia = idx - nb;
-  if (!At || ia >= K * rp) return;
-  const int k = ia / rp, j = ia - k * rp;
+  const int64_t ia = idx - nb;
+  if (!At || ia >= (int64_t)K * rp) return;
+  const int64_t k = ia / rp, j = ia - k * rp;
   At[ia] = j < rA ? A[j * K + k] : (uint16_t)0;
 }
 

@@ -1,11 +1,14 @@
-"""HBM traffic per launch of the roofline GEMM from two rocprofv3 counter runs.
+"""HBM traffic per launch of a kernel from two rocprofv3 counter runs.
 
 Usage (after two runs of the same command, one per counter, on the GPU):
 
     rocprofv3 --pmc FETCH_SIZE -d <fetch_dir> -o run --output-format csv -- python3 bench.py \
         --steps 1 --warmup 0 --legs roofline,copycal --no-cpu-baseline
     rocprofv3 --pmc WRITE_SIZE -d <write_dir> ... (same command)
-    python -m bit_nf4_quantized_12_amd.pmc_traffic <fetch_dir> <write_dir> <out.json>
+    python -m bit_nf4_quantized_12_amd.pmc_traffic <fetch_dir> <write_dir> <out.json> [kernel]
+
+The kernel defaults to the benchmark step's input-gradient GEMM instance;
+out.json for the roofline is profiles/roofline_gemm_traffic_<config>.json.
 
 FETCH_SIZE / WRITE_SIZE (KiB per dispatch, summed over the L2 channels) are
 calibrated with the `copycal` leg, one elementwise pass (bf16 negation) that
@@ -24,8 +27,13 @@ import re
 import sys
 
 COPY_BYTES = 1 << 30
-ROOFLINE_KERNEL = "gemm_kernel<512, 128, false, false, true, false>"
+ROOFLINE_KERNEL = "gemm_kernel<512, 128, true, true, true, false>"
 GEMM_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "gemm.hip")
+PROFILES = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "profiles")
+
+
+def traffic_file(config):
+    return os.path.join(PROFILES, f"roofline_gemm_traffic_{config}.json")
 
 
 def gemm_source_sha():
@@ -54,11 +62,11 @@ def _mean(vals):
     return sum(vals) / len(vals) if vals else None
 
 
-def summarize(fetch_dir, write_dir):
+def summarize(fetch_dir, write_dir, kernel=ROOFLINE_KERNEL):
     res = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _per_dispatch(d, counter)
-        gemm = [v for n, v in rows if ROOFLINE_KERNEL in re.sub(r"\s+", " ", n)]
+        gemm = [v for n, v in rows if kernel in re.sub(r"\s+", " ", n)]
         copy = [v for n, v in rows if "neg_kernel" in n]
         if not gemm or not copy:
             raise SystemExit(f"{counter}: {len(gemm)} roofline launches, {len(copy)} copies found")
@@ -67,15 +75,15 @@ def summarize(fetch_dir, write_dir):
                         "copy_counter_bytes": max(copy), "factor": COPY_BYTES / max(copy)}
     f, w = res["FETCH_SIZE"], res["WRITE_SIZE"]
     traffic = f["gemm_bytes_per_launch"] * f["factor"] + w["gemm_bytes_per_launch"] * w["factor"]
-    return {"kernel": ROOFLINE_KERNEL, "gemm_source_sha256": gemm_source_sha(),
+    return {"kernel": kernel, "gemm_source_sha256": gemm_source_sha(),
             "traffic_bytes_per_launch": traffic, "fetch": f, "write": w,
             "copy_bytes": COPY_BYTES}
 
 
 def main():
-    if len(sys.argv) != 4:
+    if len(sys.argv) not in (4, 5):
         raise SystemExit(__doc__)
-    out = summarize(sys.argv[1], sys.argv[2])
+    out = summarize(sys.argv[1], sys.argv[2], *sys.argv[4:5])
     with open(sys.argv[3], "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))

@@ -118,7 +118,8 @@ int qlora_nf4_matmul(const qlora_nf4_weight* W, const void* act, int64_t M, int 
  * sizes (the larger of the two; 0 on invalid sizes). When a product has few
  * output tiles (M of a few hundred tokens), its reduction is split and the
  * float32 partial products live in the workspace; they are summed in a fixed
- * order, so results stay bit-identical from run to run. */
+ * order, so results stay bit-identical from run to run. Calls that run
+ * concurrently must not share a workspace. */
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
 
 /* LoRA linear forward on the frozen quantised weight:
@@ -132,8 +133,8 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
  * T_save: device float32 [M, r] output, or NULL. ws: device workspace of at
  * least qlora_linear_workspace_bytes(M, N, K, r) bytes, 256-byte aligned.
  * Limits: 1 <= M, 1 <= N, 64 <= K, K % 64 == 0, 1 <= r <= 256, scale finite,
- * Mp * max(N, K, rp) < 2^31 with Mp = 64 ceil(M / 64), rp = 64 ceil(r / 64)
- * (32-bit indexing of every operand). Errors: NULL, SHAPE, ALIGN, UNSUPPORTED,
+ * max(Mp, rp) * max(N, K, rp) < 2^31 with Mp = 64 ceil(M / 64),
+ * rp = 64 ceil(r / 64) (32-bit indexing of every operand). Errors: NULL, SHAPE, ALIGN, UNSUPPORTED,
  * WORKSPACE, DEVICE. */
 int qlora_linear_fwd(const qlora_nf4_weight* W, const void* X, const void* A,
                      const void* B, int64_t M, int64_t r, float scale, void* Y,
@@ -227,6 +228,23 @@ int qlora_dequant_4bit(const uint8_t* codes, const void* consts, const float* c1
  * plus UNSUPPORTED for a codebook or double_quant out of range. */
 int qlora_4bit_matmul(const qlora_4bit_weight* W, const void* act, int64_t M, int transposed,
                       void* out, void* stream);
+
+/* The base product with a rank term fused into its epilogue:
+ *   transposed = 0:  out = act W~^T + L R^T   (act [M, K], out [M, N])
+ *   transposed = 1:  out = act W~   + L R^T   (act [M, N], out [M, K])
+ * L [M, rp] and R [Nout, rp] are bf16 (Nout = N, or K when transposed), rp a
+ * multiple of 64; float32 accumulation of both products, one bf16 rounding.
+ * This is the kernel the linear layer runs from 17 tokens on: the forward's
+ * epilogue adds (scale T) B^T and the input gradient's (scale U) A ([P1]
+ * "Low-Rank Adaptation (LoRA)"; [P2] "Method" for the bf16 product); callers
+ * that hold their own rank factors, and timing of the fused GEMM alone, use it
+ * directly. One kernel launch, no workspace (the reduction is never split
+ * here). W: host struct of device views (K % 64 == 0); act, L, R, out:
+ * device, 16-byte aligned, row-major, contiguous. Limits as qlora_nf4_matmul
+ * plus 64 <= rp <= 4096, rp % 64 == 0, max(M, Nout) rp < 2^31.
+ * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED, DEVICE. */
+int qlora_4bit_matmul_lora(const qlora_4bit_weight* W, const void* act, int64_t M, int transposed,
+                           const void* L, const void* R, int64_t rp, void* out, void* stream);
 int qlora_linear_fwd_4bit(const qlora_4bit_weight* W, const void* X, const void* A,
                           const void* B, int64_t M, int64_t r, float scale, void* Y,
                           float* T_save, void* ws, size_t ws_bytes, void* stream);

@@ -122,6 +122,25 @@ def test_linear_fwd_validation(lib):
     assert call(args(W=ctypes.byref(wsm), M=mmax + 1, r=8)) == SHAPE
 
 
+def test_rank_side_index_limit(lib):
+    """The rank side is indexed like the token side: with few tokens and a rank
+    above 64 ceil(M / 64), rp * max(N, K) must also stay below 2^31 (B^T [r, N],
+    A^T [K, rp] and the gradient partials [rp, N] are 32-bit indexed)."""
+    N, K = 1 << 24, 64
+    assert lib.qlora_linear_workspace_bytes(1, N, K, 64) > 0        # 64 * 2^24 = 2^30
+    assert lib.qlora_linear_workspace_bytes(1, N, K, 256) == 0      # 256 * 2^24 = 2^32
+    assert lib.qlora_linear_workspace_bytes(1, N, K, 128) == 0       # 128 * 2^24 = 2^31
+    assert lib.qlora_linear_workspace_bytes(1, N - 64, K, 128) > 0
+    assert lib.qlora_linear_grouped_workspace_bytes(1, N, K, 64, 4) == 0  # total rank 256
+    w = _w(N, K)
+    big = 1 << 40
+    st = lib.qlora_linear_fwd(ctypes.byref(w), FAKE, FAKE, FAKE, 1, 256, 1.0, FAKE, None, FAKE * 16, big, None)
+    assert st == SHAPE
+    st = lib.qlora_linear_bwd(ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, None, 1, 256, 1.0, FAKE, FAKE, FAKE,
+                              FAKE * 16, big, None)
+    assert st == SHAPE
+
+
 def test_linear_bwd_validation(lib):
     f = lib.qlora_linear_bwd
     w = _w(128, 128)
@@ -273,3 +292,23 @@ def test_quantize_batch_validation(lib):
     assert f(2, ok, (ctypes.c_int64 * 2)(64, 0), 0, 1, ok, ok, ok, None) == SHAPE
     assert f(2, arr(FAKE, FAKE + 2), n, 0, 1, ok, ok, ok, None) == ALIGN
     assert f(2, ok, n, 0, 1, arr(FAKE, None), ok, ok, None) == NULL
+
+
+def test_matmul_lora_validation(lib):
+    f = lib.qlora_4bit_matmul_lora
+    w = q._Weight4bit(FAKE, FAKE, FAKE, 128, 128, 0, 1)
+    W = ctypes.byref(w)
+    assert f(None, FAKE, 4, 0, FAKE, FAKE, 64, FAKE, None) == NULL
+    assert f(W, FAKE, 4, 0, None, FAKE, 64, FAKE, None) == NULL
+    assert f(W, FAKE, 4, 0, FAKE, None, 64, FAKE, None) == NULL
+    assert f(W, None, 4, 0, FAKE, FAKE, 64, FAKE, None) == NULL
+    assert f(W, FAKE, 4, 0, FAKE, FAKE, 65, FAKE, None) == SHAPE      # rp % 64 != 0
+    assert f(W, FAKE, 4, 0, FAKE, FAKE, 0, FAKE, None) == SHAPE
+    assert f(W, FAKE, 4, 0, FAKE, FAKE, 4160, FAKE, None) == SHAPE    # rp > 4096
+    assert f(W, FAKE, 0, 0, FAKE, FAKE, 64, FAKE, None) == SHAPE
+    assert f(W, FAKE, 4, 2, FAKE, FAKE, 64, FAKE, None) == UNSUPPORTED
+    assert f(W, FAKE, 4, 0, FAKE + 8, FAKE, 64, FAKE, None) == ALIGN
+    assert f(W, FAKE, 4, 0, FAKE, FAKE + 2, 64, FAKE, None) == ALIGN
+    assert f(W, FAKE, 1 << 24, 0, FAKE, FAKE, 128, FAKE, None) == SHAPE  # M rp = 2^31
+    w5 = q._Weight4bit(FAKE, FAKE, FAKE, 128, 128, 5, 1)
+    assert f(ctypes.byref(w5), FAKE, 4, 0, FAKE, FAKE, 64, FAKE, None) == UNSUPPORTED

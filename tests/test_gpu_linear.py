@@ -188,3 +188,55 @@ def test_binding_rejects_malformed_buffers():
     Y, _ = q.qlora_linear_fwd(W, Xt, At, Bt, 1.0)  # the well-formed call still runs
     torch.cuda.synchronize()
     assert Y.shape == (16, 256)
+
+
+@pytest.mark.parametrize("M", [16, 300])
+def test_autograd_wrapper_non_contiguous_input(M):
+    """LoRALinear4bitFunction on a transposed (non-contiguous) X: the forward
+    equals qlora_linear_fwd on the contiguous copy, and the backward (which
+    gets the contiguous copy the forward used) equals qlora_linear_bwd."""
+    report(f"autograd wrapper: M={M}, X a transposed view")
+    case = synth.linear_case(M, 320, 256, 16, cfg=108)
+    Wt, Xt, At, Bt, dYt = (case[k][0].to(DEV) for k in ("W", "X", "A", "B", "dY"))
+    W = q.quantize_weight(Wt)
+    Xv = Xt.t().contiguous().t()              # same values, column-major strides
+    assert not Xv.is_contiguous()
+    Xv.requires_grad_(True)
+    Ag = At.clone().requires_grad_(True)
+    Bg = Bt.clone().requires_grad_(True)
+    Y = q.LoRALinear4bitFunction.apply(Xv, Ag, Bg, W, 0.5)
+    Y.backward(dYt)
+    Yr, Tr = q.qlora_linear_fwd(W, Xt, At, Bt, 0.5)
+    dXr, dAr, dBr = q.qlora_linear_bwd(W, Xt, At, Bt, dYt, Tr, 0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Yr)
+    assert torch.equal(Xv.grad, dXr)
+    assert torch.equal(Ag.grad, dAr)
+    assert torch.equal(Bg.grad, dBr)
+
+
+@pytest.mark.parametrize("M,N,K,rp,transposed", [
+    (1100, 520, 2048, 64, False), (1100, 520, 2048, 192, True), (300, 1000, 640, 128, False),
+    (2048, 384, 1024, 64, True)])
+def test_matmul_lora_entry_point(M, N, K, rp, transposed):
+    """qlora_4bit_matmul_lora: act op(W~) + L R^T against the oracle's base
+    product (linear layer with zero adapters) plus the float64 rank term."""
+    report(f"matmul_lora: M={M} N={N} K={K} rp={rp} transposed={transposed}")
+    kin, nout = (N, K) if transposed else (K, N)
+    case = synth.linear_case(M, N, K, 8, cfg=109)
+    Wt = case["W"][0].to(DEV)
+    w32 = case["W"][1]
+    act_t, act = synth.normal((M, kin), 1.0, 0, (109, 1, 3))
+    l_t, l64 = synth.normal((M, rp), 0.5, 0, (109, 2, 3))
+    r_t, r64 = synth.normal((nout, rp), 0.02, 0, (109, 3, 3))
+    W = q.quantize_weight(Wt)
+    out = q.qlora_4bit_matmul_lora(W, act_t.to(DEV), l_t.to(DEV), r_t.to(DEV), transposed=transposed)
+    torch.cuda.synchronize()
+    Wo = _oracle_weight(w32)
+    za, zb = np.zeros((8, K)), np.zeros((N, 8))
+    if transposed:
+        base, _, _ = oracle.linear_bwd(np.zeros((M, K)), Wo, za, zb, act, 0.0)
+    else:
+        base, _ = oracle.linear_fwd(act, Wo, za, zb, 0.0)
+    ref = base + l64.astype(np.float64) @ r64.astype(np.float64).T
+    assert_close(bf16_bits_to_f32(out), ref, "out")

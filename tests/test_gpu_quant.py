@@ -149,3 +149,43 @@ def test_65b_class_stack_bit_exact_sampled():
                     np.testing.assert_array_equal(cg, pk, err_msg=f"{lab}: codes")
                     np.testing.assert_array_equal(c2g, oc2, err_msg=f"{lab}: c2")
                     assert c1g.view(np.uint32) == oc1.view(np.uint32)[0], f"{lab}: c1"
+
+
+@pytest.mark.parametrize("li", [0, 79])
+def test_65b_class_layer_one_batched_launch(li):
+    """The benchmark's quantise launch: one qlora_quantize_4bit_batch call over
+    a 65B-class layer's seven tensors (4 x 8192^2 + 3 x 22016x8192 weights,
+    N(0, 0.02), the benchmark's seeds; 49,408 workgroups). Every tensor's
+    first and last group and 48 seeded random groups are compared bit for bit
+    with the oracle; the whole batched result must equal the one-tensor-per-
+    launch result byte for byte."""
+    per_layer = [(8192, 8192)] * 4 + [(22016, 8192)] * 3
+    G = oracle_pool.GROUP
+    rng = np.random.default_rng(100 + li)
+    report(f"65B-class layer {li}: seven tensors in one batched quantise launch")
+    ws = [synth.device_normal_bf16(N * K, 0.02, 1_000_000 + 10 * li + j, DEV) for j, (N, K) in enumerate(per_layer)]
+    outs = q.qlora_quantize_4bit_batch(ws, "nf4", True)
+    torch.cuda.synchronize()
+    samples = []
+    for j, ((N, K), w, (codes, c2, c1)) in enumerate(zip(per_layer, ws, outs)):
+        ng = N * K // G
+        one = q.qlora_quantize_nf4_dq(w)
+        torch.cuda.synchronize()
+        for name, a, b in (("codes", codes, one[0]), ("c2", c2, one[1]), ("c1", c1, one[2])):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"tensor {j}: batched {name} differ"
+        del one
+        gs = np.unique(np.concatenate([[0, ng - 1], rng.choice(ng, 48, replace=False)]))
+        gi = torch.from_numpy(gs).to(DEV)
+        wg = w.view(ng, G)[gi].float().cpu().numpy()
+        cg = codes.view(ng, G // 2)[gi].cpu().numpy()
+        c2g = c2.view(ng, 256)[gi].cpu().numpy()
+        c1g = c1[gi].cpu().numpy()
+        for t in range(gs.size):
+            samples.append((f"layer {li} tensor {j} group {int(gs[t])}", wg[t], cg[t], c2g[t], c1g[t]))
+    del ws, outs
+    with oracle_pool.make_pool() as pool:
+        want = oracle_pool.quantize_slices(pool, [smp[1] for smp in samples])
+    for (lab, _, cg, c2g, c1g), (pk, oc2, oc1) in zip(samples, want):
+        np.testing.assert_array_equal(cg, pk, err_msg=f"{lab}: codes")
+        np.testing.assert_array_equal(c2g, oc2, err_msg=f"{lab}: c2")
+        assert c1g.view(np.uint32) == oc1.view(np.uint32)[0], f"{lab}: c1"
