@@ -8,10 +8,11 @@
 // LoRA side follows "QLoRA: Efficient Fine-Tuning of Quantized Language
 // Models" (mbrenndoerfer.com), section "Low-Rank Adaptation (LoRA)".
 //
-// Tile BM x BN outputs (256 x 256, or 512 x 128 for large M), 64-deep
-// reduction steps (one NF4 block), 8 wave64 in (BM / 128) x (BN / 64), each
-// wave 128 x 64 outputs = 8 x 4 v_mfma_f32_16x16x32_bf16 tiles (128 float32
-// accumulators per lane), two waves per SIMD: while one wave keeps the matrix
+// Tile BM x BN outputs (256 x 256, or 512 x 128 for large M, or 128 x 128
+// when even 256 x 256 leaves most CUs idle), 64-deep reduction steps (one NF4
+// block), 8 wave64 in (BM / WM) x (BN / 64), each wave WM x 64 outputs
+// (WM = 128: 8 x 4 v_mfma_f32_16x16x32_bf16 tiles, 128 float32 accumulators
+// per lane; WM = 32 for the 128 x 128 tile), two waves per SIMD: while one wave keeps the matrix
 // core busy the other issues its unpacking VALU work. The unpack work per
 // step grows with BN and the MFMA work with BM x BN, so the 512 x 128 tile
 // halves the unpacking per MFMA at the same LDS read volume per step. LDS
@@ -182,9 +183,11 @@ typedef __attribute__((address_space(1))) void gbl_void_t;
 template <int BM, int BN, bool TW, bool LORA, bool VEC, bool ABS>
 __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
   constexpr int WN = BN / 64;        // waves along the output columns
+  constexpr int WM = BM * WN / 8;    // output rows per wave (8 waves)
+  constexpr int MI = WM / 16;        // 16-row MFMA tiles per wave
   constexpr int QW = BN / 64;        // code words unpacked per thread per step
   constexpr int XJ = BM / 64;        // activation LDS-DMA instructions per wave per step
-  static_assert((BM / 128) * WN == NT / 64, "8 waves of 128 x 64");
+  static_assert((BM / WM) * WN == NT / 64 && WM % 16 == 0, "8 waves of WM x 64");
   extern __shared__ __align__(16) uint16_t smem[];
   uint16_t* sA = smem;                // [2][BM * 64] activation tiles
   uint16_t* sB = smem + 2 * BM * 64;  // [2][BN * 64] weight tiles
@@ -280,9 +283,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
     return h;
   };
 
-  f32x4 acc[8][4];
+  f32x4 acc[MI][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -294,7 +297,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
   __builtin_amdgcn_s_waitcnt(0);  // stage 0 LDS-DMA landed (vmcnt = lgkmcnt = 0)
   __syncthreads();
 
-  const int arow = wm * 128 + (l & 15);
+  const int arow = wm * WM + (l & 15);
   const int brow = wn * 64 + (l & 15);
   // logical chunk of a fragment: 4 kk + (l >> 4); all fragment rows of a
   // lane share swz(row) = swz(l & 15)
@@ -316,7 +319,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) b[j] = lds_load8(reinterpret_cast<const __bf16*>(b_s + (brow + 16 * j) * 64 + ck));
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < MI; ++i) {
         const bf16x8 a = lds_load8(reinterpret_cast<const __bf16*>(a_s + (arow + 16 * i) * 64 + ck));
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a, b[j], acc[i][j]);
@@ -362,7 +365,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) b[j] = lds_load8(reinterpret_cast<const __bf16*>(sB + (brow + 16 * j) * 64 + ck));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < MI; ++i) {
           const bf16x8 a = lds_load8(reinterpret_cast<const __bf16*>(sA + (arow + 16 * i) * 64 + ck));
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a, b[j], acc[i][j]);
@@ -375,14 +378,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
   // D layout of a 16 x 16 tile: lane holds rows 4 (l >> 4) + v, column l & 15
   float* __restrict__ part = p.ksplit > 1 ? p.part + (int64_t)ksp * p.M * p.Nout : nullptr;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int col = n0 + wn * 64 + 16 * j + (l & 15);
       if (col >= p.Nout) continue;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int row = m0 + wm * 128 + 16 * i + 4 * (l >> 4) + v;
+        const int row = m0 + wm * WM + 16 * i + 4 * (l >> 4) + v;
         if (row < p.M) {
           if (part) {
             part[(int64_t)row * p.Nout + col] = acc[i][j][v];
@@ -437,14 +440,19 @@ hipError_t launch_variant(const GemmParams& p, hipStream_t s) {
 
 template <bool TW, bool LORA, bool ABS>
 hipError_t launch_rows(const GemmParams& p, hipStream_t s) {
-  // reductions in whole 64-element steps take the DMA / uniform-address
-  // path; from 1024 rows on the 512 x 128 tile (half the unpacking per MFMA)
+  // reductions in whole 64-element steps take the DMA / uniform-address path
   const bool vec = p.Kred % BK == 0;
-  if (p.M >= 1024)
-    return vec ? launch_variant<512, 128, TW, LORA, true, ABS>(p, s)
-               : launch_variant<512, 128, TW, LORA, false, ABS>(p, s);
-  return vec ? launch_variant<256, 256, TW, LORA, true, ABS>(p, s)
-             : launch_variant<256, 256, TW, LORA, false, ABS>(p, s);
+  switch (gemm_tile(p.M, p.Nout)) {
+    case kTile512x128:
+      return vec ? launch_variant<512, 128, TW, LORA, true, ABS>(p, s)
+                 : launch_variant<512, 128, TW, LORA, false, ABS>(p, s);
+    case kTile256x256:
+      return vec ? launch_variant<256, 256, TW, LORA, true, ABS>(p, s)
+                 : launch_variant<256, 256, TW, LORA, false, ABS>(p, s);
+    default:
+      return vec ? launch_variant<128, 128, TW, LORA, true, ABS>(p, s)
+                 : launch_variant<128, 128, TW, LORA, false, ABS>(p, s);
+  }
 }
 
 template <bool TW, bool LORA>

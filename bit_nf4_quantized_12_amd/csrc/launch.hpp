@@ -42,17 +42,29 @@ struct GemmParams {
   float* part = nullptr;
 };
 
-// Splits of the reduction for a GEMM with few output tiles: ~256 workgroups,
-// at most 8 splits of at least 4 steps each; 1 from 192 tiles on. Returns
-// the split count (every split non-empty) and the steps per split.
+// Output tile of the GEMM: 512 x 128 from 1024 rows on (half the unpacking
+// per MFMA), else 256 x 256; when that leaves fewer than 192 tiles (most of
+// the 256 CUs idle), 128 x 128.
+enum GemmTile { kTile512x128 = 0, kTile256x256 = 1, kTile128x128 = 2 };
+inline int64_t gemm_tiles(int64_t M, int64_t Nout, int64_t bm, int64_t bn) {
+  return ((M + bm - 1) / bm) * ((Nout + bn - 1) / bn);
+}
+inline GemmTile gemm_tile(int64_t M, int64_t Nout) {
+  const bool big = M >= 1024;
+  if (gemm_tiles(M, Nout, big ? 512 : 256, big ? 128 : 256) >= 192) return big ? kTile512x128 : kTile256x256;
+  return kTile128x128;
+}
+
+// Splits of the reduction: with 128 x 128 tiles, enough splits for ~256
+// workgroups, at most 4, each at least 4 steps of 64; none otherwise.
+// Returns the split count (every split non-empty) and the steps per split.
 inline int gemm_ksplit(int64_t M, int64_t Nout, int64_t Kred, int* kchunk) {
-  const int64_t BMs = M >= 1024 ? 512 : 256, BNs = M >= 1024 ? 128 : 256;
-  const int64_t tiles = ((M + BMs - 1) / BMs) * ((Nout + BNs - 1) / BNs);
   const int64_t nk = (Kred + 63) / 64;
   int64_t ks = 1;
-  if (tiles < 192) {
+  if (gemm_tile(M, Nout) == kTile128x128) {
+    const int64_t tiles = gemm_tiles(M, Nout, 128, 128);
     ks = (256 + tiles - 1) / tiles;
-    if (ks > 8) ks = 8;
+    if (ks > 4) ks = 4;
     if (ks > nk / 4) ks = nk / 4;
     if (ks < 1) ks = 1;
   }
