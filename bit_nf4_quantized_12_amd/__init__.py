@@ -102,6 +102,7 @@ def load_library(path=LIB_PATH):
             "qlora_linear_workspace_bytes": ([i64, i64, i64, i64], sz),
             "qlora_nf4_matmul": ([ctypes.POINTER(_Weight), vp, i64, i32, vp, vp], i32),
             "qlora_linear_fwd": ([ctypes.POINTER(_Weight), vp, vp, vp, i64, i64, f32, vp, vp, vp, sz, vp], i32),
+            "qlora_linear_fwd_noalloc": ([ctypes.POINTER(_Weight), vp, vp, vp, i64, i64, f32, vp, vp, vp], i32),
             "qlora_linear_bwd": ([ctypes.POINTER(_Weight), vp, vp, vp, vp, vp, i64, i64, f32, vp, vp, vp, vp, sz, vp], i32),
             "qlora_status_string": ([i32], ctypes.c_char_p),
             "qlora_levels": ([i32, ctypes.POINTER(ctypes.c_float)], i32),
@@ -407,6 +408,30 @@ def qlora_linear_fwd(W, X, A, B, scale, save_T=True, Y=None, T=None, workspace=N
     fn = getattr(load_library(), "qlora_linear_fwd" + sfx)
     _check(fn(ctypes.byref(w), _ptr(X), _ptr(A), _ptr(B), M, r, float(scale), _ptr(Y), _ptr(T), _ptr(ws),
               ws.numel(), _stream(dev)))
+    return Y, T
+
+
+def qlora_linear_fwd_noalloc(W, X, A, B, scale, Y, T=None):
+    """qlora_linear_fwd with the library's fixed scratch in place of a workspace:
+    allocates nothing (Y, and T if given, are the caller's buffers). NF4 + DQ
+    weights only; sizes needing more than 64 MiB of scratch raise QloraError."""
+    for t, name in ((X, "X"), (A, "A"), (B, "B")):
+        _need(t, torch.bfloat16, name)
+    if not _is_nf4_dq(W):
+        raise ValueError("qlora_linear_fwd_noalloc takes NF4 + double-quantised weights")
+    M, K = X.shape
+    r = A.shape[0]
+    if K != W.cols or A.shape[1] != K or B.shape != (W.rows, r):
+        raise ValueError("shape mismatch: X [M, K], A [r, K], B [N, r], W [N, K]")
+    dev = X.device
+    _same_device(dev, A=A, B=B)
+    _check_weight(W, dev)
+    _buf(Y, (M, W.rows), torch.bfloat16, dev, "Y")
+    if T is not None:
+        _buf(T, (M, r), torch.float32, dev, "T")
+    w, _ = _weight_struct(W)
+    _check(load_library().qlora_linear_fwd_noalloc(ctypes.byref(w), _ptr(X), _ptr(A), _ptr(B), M, r,
+                                                   float(scale), _ptr(Y), _ptr(T), _stream(dev)))
     return Y, T
 
 

@@ -3,6 +3,7 @@
 // The operations themselves are defined in include/qlora.h.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <new>
 
 #include "qlora.h"
@@ -14,6 +15,43 @@ using namespace qlora;
 namespace {
 
 constexpr int kGemvMaxM = 16;
+
+// Scratch of qlora_linear_fwd_noalloc, for callers that cannot allocate: one
+// copy per GPU for the life of the process. In host code `scratch` only names
+// the symbol; its device address (per device) comes from hipGetSymbolAddress
+// and is what kernels get. No forward kernel reads a scratch byte it has not
+// written in the same call, so nothing needs clearing; calls that overlap on
+// one GPU share it and race.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the scratch on the device of `stream` (which must be the
+// current device), looked up once per device.
+int scratch_address(hipStream_t stream, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return QLORA_ERR_DEVICE;
+  if (stream) {
+    int sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return QLORA_ERR_DEVICE;
+    if (sdev != dev) return QLORA_ERR_DEVICE;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return QLORA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return QLORA_ERR_DEVICE;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QLORA_OK;
+}
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -145,8 +183,9 @@ int view_4bit(const qlora_4bit_weight* W, WView& v) {
   return QLORA_OK;
 }
 
-int check_linear(const WView& W, const void* X, const void* A, const void* B,
-                 int64_t M, int64_t r, float scale, const void* ws, size_t ws_bytes) {
+// The linear layer's operand checks (no workspace).
+int check_linear_args(const WView& W, const void* X, const void* A, const void* B, int64_t M, int64_t r,
+                      float scale) {
   if (!X || !A || !B) return QLORA_ERR_NULL;
   const int64_t N = W.N, K = W.K;
   if (M < 1 || N < 1 || K < 64 || (K % 64) != 0) return QLORA_ERR_SHAPE;
@@ -154,6 +193,13 @@ int check_linear(const WView& W, const void* X, const void* A, const void* B,
   if (!index_fits(M, N, K, r) || N * K >= (int64_t(1) << 40)) return QLORA_ERR_SHAPE;
   if (!std::isfinite(scale)) return QLORA_ERR_UNSUPPORTED;
   if (!aligned(X, 16) || !aligned(A, 16) || !aligned(B, 16)) return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+int check_linear(const WView& W, const void* X, const void* A, const void* B,
+                 int64_t M, int64_t r, float scale, const void* ws, size_t ws_bytes) {
+  const int st = check_linear_args(W, X, A, B, M, r, scale);
+  if (st != QLORA_OK) return st;
   if (!ws) return QLORA_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return QLORA_ERR_ALIGN;
   (void)ws_bytes;
@@ -593,6 +639,7 @@ const char* qlora_status_string(int status) {
     case QLORA_ERR_UNSUPPORTED: return "unsupported mode or value";
     case QLORA_ERR_WORKSPACE: return "workspace missing or too small";
     case QLORA_ERR_DEVICE: return "HIP call failed";
+    case QLORA_ERR_SCRATCH: return "sizes need more than the library's fixed scratch (qlora_linear_fwd_noalloc)";
     default: return "unknown status";
   }
 }
@@ -806,6 +853,24 @@ int qlora_linear_fwd(const qlora_nf4_weight* W, const void* X, const void* A, co
   WView v;
   const int st = view_nf4(W, v);
   return st != QLORA_OK ? st : fwd_impl(v, X, A, B, M, r, scale, Y, T_save, ws, ws_bytes, stream);
+}
+
+int qlora_linear_fwd_noalloc(const qlora_nf4_weight* W, const void* X, const void* A, const void* B,
+                             int64_t M, int64_t r, float scale, void* Y, float* T_save, void* stream) {
+  WView v;
+  int st = view_nf4(W, v);
+  if (st != QLORA_OK) return st;
+  // every argument check of the workspace form, and the size limit, before
+  // any HIP call
+  st = check_linear_args(v, X, A, B, M, r, scale);
+  if (st != QLORA_OK) return st;
+  if (!Y) return QLORA_ERR_NULL;
+  if (!aligned(Y, 16) || (T_save && !aligned(T_save, 4))) return QLORA_ERR_ALIGN;
+  if (plan(M, v.N, v.K, r).fwd_total > kScratchBytes) return QLORA_ERR_SCRATCH;
+  void* ptr = nullptr;
+  st = scratch_address(static_cast<hipStream_t>(stream), &ptr);
+  if (st != QLORA_OK) return st;
+  return fwd_impl(v, X, A, B, M, r, scale, Y, T_save, ptr, kScratchBytes, stream);
 }
 
 int qlora_linear_fwd_4bit(const qlora_4bit_weight* W, const void* X, const void* A, const void* B,

@@ -55,7 +55,9 @@ typedef enum {
   QLORA_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned           */
   QLORA_ERR_UNSUPPORTED = 4, /* a valid but unsupported mode or value      */
   QLORA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than needed   */
-  QLORA_ERR_DEVICE = 6       /* a HIP call failed (launch or device query) */
+  QLORA_ERR_DEVICE = 6,      /* a HIP call failed (launch or device query) */
+  QLORA_ERR_SCRATCH = 7      /* sizes need more than the fixed scratch of
+                                qlora_linear_fwd_noalloc                  */
 } qlora_status;
 
 typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
@@ -139,6 +141,22 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
 int qlora_linear_fwd(const qlora_nf4_weight* W, const void* X, const void* A,
                      const void* B, int64_t M, int64_t r, float scale, void* Y,
                      float* T_save, void* ws, size_t ws_bytes, void* stream);
+
+/* qlora_linear_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The library's own scratch takes the
+ * workspace's place: a fixed 64 MiB array per GPU, held from the library's
+ * load until the process ends; this call allocates nothing and frees nothing.
+ * Sizes whose forward workspace (qlora_linear_workspace_bytes covers it)
+ * exceeds 64 MiB return QLORA_ERR_SCRATCH before any HIP call. `stream` must
+ * belong to the current device (else QLORA_ERR_DEVICE). Every call on a GPU
+ * shares that GPU's scratch, so calls that overlap in time on one GPU (other
+ * streams, other host threads) race; calls ordered on one stream do not.
+ * Results are those of qlora_linear_fwd bit for bit. Other arguments, limits
+ * and errors as for qlora_linear_fwd. */
+int qlora_linear_fwd_noalloc(const qlora_nf4_weight* W, const void* X, const void* A,
+                             const void* B, int64_t M, int64_t r, float scale, void* Y,
+                             float* T_save, void* stream);
 
 /* Backward of qlora_linear_fwd for the upstream gradient dY [M, N] (bf16).
  * [P2] abstract: gradients flow through the frozen 4-bit weight into the

@@ -17,7 +17,7 @@ import oracle
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qlora.h")
 
-OK, NULL, SHAPE, ALIGN, UNSUPPORTED, WORKSPACE, DEVICE = range(7)
+OK, NULL, SHAPE, ALIGN, UNSUPPORTED, WORKSPACE, DEVICE, SCRATCH = range(8)
 FAKE = 0x10000  # an aligned address that is never touched by validation failures
 
 
@@ -41,7 +41,7 @@ def test_levels_bit_exact_with_oracle():
 
 
 def test_status_strings(lib):
-    for s in range(7):
+    for s in range(8):
         assert lib.qlora_status_string(s)
     assert lib.qlora_status_string(99) == b"unknown status"
 
@@ -312,3 +312,24 @@ def test_matmul_lora_validation(lib):
     assert f(W, FAKE, 1 << 24, 0, FAKE, FAKE, 128, FAKE, None) == SHAPE  # M rp = 2^31
     w5 = q._Weight4bit(FAKE, FAKE, FAKE, 128, 128, 5, 1)
     assert f(ctypes.byref(w5), FAKE, 4, 0, FAKE, FAKE, 64, FAKE, None) == UNSUPPORTED
+
+
+def test_fwd_noalloc_validation(lib):
+    """qlora_linear_fwd_noalloc rejects bad arguments, and sizes whose forward
+    workspace exceeds its fixed 64 MiB scratch, before any HIP call."""
+    f = lib.qlora_linear_fwd_noalloc
+    w = _w(4096, 4096)
+    W = ctypes.byref(w)
+    assert f(None, FAKE, FAKE, FAKE, 4, 8, 1.0, FAKE, None, None) == NULL
+    assert f(W, None, FAKE, FAKE, 4, 8, 1.0, FAKE, None, None) == NULL
+    assert f(W, FAKE, FAKE, FAKE, 4, 8, 1.0, None, None, None) == NULL
+    assert f(W, FAKE, FAKE, FAKE, 0, 8, 1.0, FAKE, None, None) == SHAPE
+    assert f(W, FAKE, FAKE, FAKE, 4, 300, 1.0, FAKE, None, None) == SHAPE
+    assert f(W, FAKE, FAKE, FAKE, 4, 8, math.nan, FAKE, None, None) == UNSUPPORTED
+    assert f(W, FAKE + 2, FAKE, FAKE, 4, 8, 1.0, FAKE, None, None) == ALIGN
+    assert f(W, FAKE, FAKE, FAKE, 4, 8, 1.0, FAKE + 8, None, None) == ALIGN
+    assert f(W, FAKE, FAKE, FAKE, 4, 8, 1.0, FAKE, FAKE + 2, None) == ALIGN
+    # 65536 tokens at rank 256: partials, T and bf16(s T) need 160 MiB of scratch
+    assert lib.qlora_linear_workspace_bytes(65536, 4096, 4096, 256) > (64 << 20)
+    assert f(W, FAKE, FAKE, FAKE, 65536, 256, 1.0, FAKE, None, None) == SCRATCH
+    assert lib.qlora_status_string(SCRATCH) != b"unknown status"
