@@ -113,8 +113,18 @@ __device__ __forceinline__ int tile_off(int R, int c) { return R * 64 + 8 * (c ^
 template <int QW>
 struct WPart {
   uint32_t c[QW];
-  float chat;
+  float g;       // c1 of the block's group, or the block's fp32 absmax (no DQ)
+  uint32_t c2b;  // E4M3 byte of the block constant (double quantisation)
+  bool ok;       // false: codes past the reduction end (their c^ is 0)
 };
+
+// The block constant c^ of a WPart, decoded when the codes are unpacked (not
+// when they are loaded, so that the loads can stay in flight).
+template <bool ABS, int QW>
+__device__ __forceinline__ float wpart_chat(const WPart<QW>& h) {
+  const float c = ABS ? h.g : __fmul_rn(e4m3_value(h.c2b), h.g);
+  return h.ok ? c : 0.0f;
+}
 
 // Thread -> weight codes of a step (QW words = 8 QW codes; TPR = 8 / QW
 // threads share a block). Forward: thread t owns tile row t / TPR (weight
@@ -159,8 +169,9 @@ __device__ __forceinline__ void store_wword(uint32_t word, int q, const BlockTab
 }
 
 template <bool TW, int QW>
-__device__ __forceinline__ void store_wpart(const WPart<QW>& h, const Levels& lv, uint16_t* __restrict__ dst, int tid) {
-  const BlockTable t = make_table(h.chat, lv);
+__device__ __forceinline__ void store_wpart(const WPart<QW>& h, float chat, const Levels& lv,
+                                            uint16_t* __restrict__ dst, int tid) {
+  const BlockTable t = make_table(chat, lv);
 #pragma unroll
   for (int q = 0; q < QW; ++q) store_wword<TW, QW>(h.c[q], q, t, dst, tid);
 }
@@ -265,7 +276,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
       const int ke = min(kt, nk - 1);
       const int64_t e = (int64_t)ke * wstep + wbase;
       load_words<QW>(p.codes, e, h.c);
-      h.chat = block_const<ABS>(p.c2, p.c1, p.absmax, e >> 6);
+      if (ABS) {
+        h.g = p.absmax[e >> 6];
+      } else {
+        h.c2b = p.c2[e >> 6];
+        h.g = p.c1[e >> 14];
+      }
+      h.ok = true;
     } else {
       // general reduction length: codes past the reduction end get c^ = 0
       // (their unpacked weights are exact zeros, which zero the reduction
@@ -277,8 +294,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
       col = min(col, p.wK - 8 * QW);
       const int64_t e = n * p.wK + col;
       load_words<QW>(p.codes, e, h.c);
-      const float chat = block_const<ABS>(p.c2, p.c1, p.absmax, e >> 6);
-      h.chat = ok ? chat : 0.0f;
+      if (ABS) {
+        h.g = p.absmax[e >> 6];
+      } else {
+        h.c2b = p.c2[e >> 6];
+        h.g = p.c1[e >> 14];
+      }
+      h.ok = ok;
     }
     return h;
   };
@@ -291,9 +313,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
 
   // prologue: stage 0 complete, codes of the next step in flight
   load_x(kbeg, 0);
-  WPart<QW> wnext = load_w(kbeg);
-  store_wpart<TW, QW>(wnext, p.lv, sB, tid);
-  wnext = load_w(kbeg + 1);
+  WPart<QW> w0 = load_w(kbeg), w1;
+  store_wpart<TW, QW>(w0, wpart_chat<ABS>(w0), p.lv, sB, tid);
+  w1 = load_w(kbeg + 1);
   __builtin_amdgcn_s_waitcnt(0);  // stage 0 LDS-DMA landed (vmcnt = lgkmcnt = 0)
   __syncthreads();
 
@@ -304,11 +326,24 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
   const int ck0 = 8 * ((0 + (l >> 4)) ^ swz(l & 15));
   const int ck1 = 8 * ((4 + (l >> 4)) ^ swz(l & 15));
 
-  for (int kt = kbeg; kt < kend; ++kt) {
-    const int st = (kt - kbeg) & 1;
+  // Step kt (stage st): the activation LDS-DMA of step kt + 1, the code loads
+  // of step kt + 2 into `next`, the MFMAs of step kt, and the unpack of `cur`
+  // (the codes of step kt + 1, loaded a step earlier) into the other stage.
+  // With the small tile (few output tiles: a few hundred tokens, short steps)
+  // the code loads stay in flight across the step's barrier: a scheduling
+  // barrier keeps them after the DMA, so the end-of-step vmcnt(NCODE) waits
+  // for the DMA only, and the loop is unrolled by two so that the two code
+  // buffers alternate in fixed registers (a copy would wait for the loads).
+  // The large tiles have no registers to spare for that (it spills) and wait
+  // for everything at the end of each step.
+  constexpr bool KEEP = WM == 32 && VEC;
+  constexpr int NCODE = ABS ? 2 : 3;  // code words + block constant(s)
+  constexpr int kStepWait = KEEP ? (NCODE | (7 << 4)) : 0;  // vmcnt(NCODE), expcnt any, lgkmcnt(0)
+  auto step = [&](int kt, int st, WPart<QW>& next, const WPart<QW>& cur) {
     load_x(kt + 1, st ^ 1);
-    const WPart<QW> wcur = wnext;
-    wnext = load_w(kt + 2);
+    if (KEEP) __builtin_amdgcn_sched_barrier(0);
+    next = load_w(kt + 2);
+    if (KEEP) __builtin_amdgcn_sched_barrier(0);
 
     const uint16_t* a_s = sA + st * BM * 64;
     const uint16_t* b_s = sB + st * BN * 64;
@@ -327,10 +362,24 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
     }
     // unpack the next weight tile into the other stage (free since the last
     // barrier); steps past the end unpack a clamped block into an unused stage
-    store_wpart<TW, QW>(wcur, p.lv, sB + (st ^ 1) * BN * 64, tid);
-    __builtin_amdgcn_s_waitcnt(0);  // this step's LDS-DMA and LDS writes are complete
-    __syncthreads();
+    store_wpart<TW, QW>(cur, wpart_chat<ABS>(cur), p.lv, sB + (st ^ 1) * BN * 64, tid);
+    __builtin_amdgcn_s_waitcnt(kStepWait);  // this step's LDS-DMA and LDS writes are complete
+    __builtin_amdgcn_s_barrier();
+  };
+  if (KEEP) {
+    int kt = kbeg;
+    for (; kt + 1 < kend; kt += 2) {
+      step(kt, 0, w0, w1);
+      step(kt + 1, 1, w1, w0);
+    }
+    if (kt < kend) step(kt, 0, w0, w1);
+  } else {
+    for (int kt = kbeg; kt < kend; ++kt) {
+      step(kt, (kt - kbeg) & 1, w0, w1);
+      w1 = w0;
+    }
   }
+  __builtin_amdgcn_s_waitcnt(0);
 
   if (LORA && ksp == 0) {
     // acc += lora_l[rows, :] lora_r[cols, :]^T, 64 rank columns per step
