@@ -1,5 +1,5 @@
-// Few-token forward (M <= 16): Y = X W~^T + s T B^T with T = X A^T, in one
-// launch, bound by reading the 4-bit weight from HBM.
+// Few-token forward (M <= 16): Y = X W~^T + s T B^T with T = X A^T, bound by
+// reading the 4-bit weight from HBM.
 //
 // "QLoRA: Efficient Finetuning of Quantized LLMs" (inquiringlines.com),
 // "Method": dequantise to BFloat16, multiply in 16-bit. The LoRA term follows
