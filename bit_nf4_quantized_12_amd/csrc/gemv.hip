@@ -118,20 +118,39 @@ struct FewTokParams {
 
 namespace {
 
+// Sum over the 64 lanes of a wave in a fixed butterfly order: xor 1 and 2
+// inside quads, the half-row and row mirrors (lane i with 7 - i, then with
+// 15 - i), then xor 16 and 32. Every step adds two values whose order does
+// not matter (a + b == b + a), so all lanes end with the same bits, the
+// same on every run.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
 // Producer: T[m][j] = sum_k X[m][k] A[j][k] for j in [j0, j0 + J) (J <= 16),
 // m < M. Per column j and group of up to 8 tokens, thread t takes the
 // 8-column chunks t, t + FT_NT, .. (the A chunk and the tokens' X chunks in
-// flight together), multiplies in float32 (bf16 products are exact), and the
-// FT_NT partial sums of each (m, j) are added by a fixed-order tree in LDS.
-// The T-only launch of the backward runs this same code.
+// flight together) and multiplies in float32 (bf16 products are exact); the
+// FT_NT partial sums of each (m, j) are added in a fixed order: within each
+// wave in registers (wave_sum), then the 8 wave sums in wave order. The
+// T-only launch of the backward runs this same code.
 constexpr int FT_PM = 8;  // tokens per pass
+constexpr int FT_W = FT_NT / 64;
 __device__ void ft_produce(const FewTokParams& p, int j0, float* red) {
   const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63;
   const int nch = p.K >> 3;
   const int nj = min(p.J, p.R - j0);
   for (int jj = 0; jj < nj; ++jj) {
     const uint16_t* arow = p.A + (int64_t)(j0 + jj) * p.K;
     for (int m0 = 0; m0 < p.M; m0 += FT_PM) {
+      const int mc = min(FT_PM, p.M - m0);  // tokens in this pass (uniform)
       float acc[FT_PM];
 #pragma unroll
       for (int i = 0; i < FT_PM; ++i) acc[i] = 0.0f;
@@ -140,10 +159,11 @@ __device__ void ft_produce(const FewTokParams& p, int j0, float* red) {
         uint4 xv[FT_PM];
 #pragma unroll
         for (int i = 0; i < FT_PM; ++i)
-          xv[i] = *reinterpret_cast<const uint4*>(p.X + (int64_t)min(m0 + i, p.M - 1) * p.K + 8 * ch);
+          if (i < mc) xv[i] = *reinterpret_cast<const uint4*>(p.X + (int64_t)(m0 + i) * p.K + 8 * ch);
         const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
 #pragma unroll
         for (int i = 0; i < FT_PM; ++i) {
+          if (i >= mc) continue;
           const uint32_t xw[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
           float a = acc[i];
 #pragma unroll
@@ -154,26 +174,29 @@ __device__ void ft_produce(const FewTokParams& p, int j0, float* red) {
           acc[i] = a;
         }
       }
-      // fixed-order tree over the FT_NT threads
 #pragma unroll
-      for (int i = 0; i < FT_PM; ++i) red[i * FT_NT + tid] = acc[i];
-      __syncthreads();
-      for (int h = FT_NT / 2; h > 0; h >>= 1) {
-        if (tid < h) {
+      for (int i = 0; i < FT_PM; ++i)
+        if (i < mc) acc[i] = wave_sum(acc[i]);
+      if (l == 0) {
 #pragma unroll
-          for (int i = 0; i < FT_PM; ++i) red[i * FT_NT + tid] += red[i * FT_NT + tid + h];
-        }
-        __syncthreads();
+        for (int i = 0; i < FT_PM; ++i)
+          if (i < mc) red[i * FT_W + w] = acc[i];
       }
-      if (tid < FT_PM && m0 + tid < p.M) p.T[(int64_t)(m0 + tid) * p.R + j0 + jj] = red[tid * FT_NT];
       __syncthreads();
+      if (tid < mc) {
+        float t = red[tid * FT_W];
+#pragma unroll
+        for (int v = 1; v < FT_W; ++v) t += red[tid * FT_W + v];
+        p.T[(int64_t)(m0 + tid) * p.R + j0 + jj] = t;
+      }
+      __syncthreads();  // red is reused by the next pass
     }
   }
 }
 
 // T = X A^T: workgroup w computes columns w J .. w J + J - 1.
 __global__ __launch_bounds__(FT_NT) void fewtok_t_kernel(FewTokParams p) {
-  __shared__ float pred[FT_PM * FT_NT];
+  __shared__ float pred[FT_PM * FT_W];
   ft_produce(p, blockIdx.x * p.J, pred);
 }
 
