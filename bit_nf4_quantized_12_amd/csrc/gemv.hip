@@ -134,13 +134,13 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // Producer: T[m][j] = sum_k X[m][k] A[j][k] for j in [j0, j0 + J) (J <= 16),
-// m < M. Per column j and group of up to 8 tokens, thread t takes the
+// m < M. Per column j and group of up to 16 tokens, thread t takes the
 // 8-column chunks t, t + FT_NT, .. (the A chunk and the tokens' X chunks in
 // flight together) and multiplies in float32 (bf16 products are exact); the
 // FT_NT partial sums of each (m, j) are added in a fixed order: within each
 // wave in registers (wave_sum), then the 8 wave sums in wave order. The
 // T-only launch of the backward runs this same code.
-constexpr int FT_PM = 8;  // tokens per pass
+constexpr int FT_PM = 16;  // tokens per pass (M <= 16: one pass)
 constexpr int FT_W = FT_NT / 64;
 __device__ void ft_produce(const FewTokParams& p, int j0, float* red) {
   const int tid = threadIdx.x;
@@ -157,9 +157,10 @@ __device__ void ft_produce(const FewTokParams& p, int j0, float* red) {
       for (int ch = tid; ch < nch; ch += FT_NT) {
         const uint4 av = *reinterpret_cast<const uint4*>(arow + 8 * ch);
         uint4 xv[FT_PM];
+        const uint16_t* xp = p.X + (int64_t)m0 * p.K + 8 * ch;
 #pragma unroll
-        for (int i = 0; i < FT_PM; ++i)
-          if (i < mc) xv[i] = *reinterpret_cast<const uint4*>(p.X + (int64_t)(m0 + i) * p.K + 8 * ch);
+        for (int i = 0; i < FT_PM; ++i, xp += p.K)
+          if (i < mc) xv[i] = *reinterpret_cast<const uint4*>(xp);
         const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
 #pragma unroll
         for (int i = 0; i < FT_PM; ++i) {
