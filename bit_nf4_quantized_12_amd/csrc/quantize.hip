@@ -48,6 +48,19 @@ __device__ __forceinline__ float div_block(float w, float c, float r, bool fast)
   return w / c;
 }
 
+// r = RN32(1 / c) for a block max c in [2^-100, 2^100] (a bf16 value: at most
+// 8 significant bits): the hardware reciprocal (within 1 ulp) refined by one
+// Newton step through fused multiply-adds, e = 1 - c y0 being exact. Checked
+// exhaustively over the 128 bf16 significands (the step commutes with
+// power-of-two scaling inside that range), it is correctly rounded even from
+// a start 2 ulps away; it replaces an IEEE division (about 10 instructions)
+// per block and lane.
+__device__ __forceinline__ float rcp_bf16(float c) {
+  const float y0 = __builtin_amdgcn_rcpf(c);
+  const float e = __builtin_fmaf(-c, y0, 1.0f);
+  return __builtin_fmaf(e, y0, y0);
+}
+
 // |x| <= 1, so the cell is in [0, 2 scale] (a NaN converts to cell 0)
 __device__ __forceinline__ uint32_t nearest_code(float x, const float2* __restrict__ tab, float scale) {
   const int cell = (int)__builtin_fmaf(x, scale, scale);
@@ -131,7 +144,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantBatch bt, QuantTable
     // exact zero like any x = 0
     const float md = m > 0.0f ? m : 1.0f;
     const bool fast = md >= 0x1p-100f && md <= 0x1p100f;
-    const float r = 1.0f / md;
+    const float r = rcp_bf16(md);  // used by the lanes with `fast` only
     uint32_t word = 0;
     if (__all(fast)) {
       // every block of the wave in range (wave-uniform branch): the
