@@ -22,11 +22,15 @@ namespace {
 
 __device__ __forceinline__ float dpp_max8(float v) {
   // lanes of one block: 8 consecutive lanes. xor 1, xor 2 inside a quad,
-  // then the mirror inside 8 lanes pairs the two quads.
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
-  return v;
+  // then the mirror inside 8 lanes pairs the two quads. v is an absolute
+  // value (finite weights), so the float order is the unsigned order of the
+  // bits and an integer max does it (one instruction per step with the DPP
+  // operand folded in, no NaN canonicalisation).
+  uint32_t u = __float_as_uint(v);
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0xB1, 0xF, 0xF, true));
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x4E, 0xF, 0xF, true));
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x141, 0xF, 0xF, true));
+  return __uint_as_float(u);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
