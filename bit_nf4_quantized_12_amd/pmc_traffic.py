@@ -14,6 +14,10 @@ SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE:
     python -m bit_nf4_quantized_12_amd.pmc_traffic table <fetch_dir> <write_dir> <kernel substring> ...
     python -m bit_nf4_quantized_12_amd.pmc_traffic mfma <run_dir> <kernel substring> ...
 
+and the mean per dispatch of every counter of a run, per kernel and grid size:
+
+    python -m bit_nf4_quantized_12_amd.pmc_traffic counters <run_dir> <kernel substring> ...
+
 The kernel defaults to the benchmark step's input-gradient GEMM instance;
 out.json for the roofline is profiles/roofline_gemm_traffic_<config>.json.
 
@@ -132,6 +136,13 @@ def mfma(run_dir, kernels):
     return out
 
 
+def counters(run_dir, kernels):
+    """Mean per dispatch of every counter in a run, per kernel and grid size."""
+    return [{"kernel": k[0], "grid": k[1], "dispatches": max(len(v) for v in cs.values()),
+             "means": {c: _mean(v) for c, v in sorted(cs.items())}}
+            for k, cs in sorted(_by_shape(run_dir, kernels).items())]
+
+
 def _mean(vals):
     return sum(vals) / len(vals) if vals else None
 
@@ -157,6 +168,9 @@ def summarize(fetch_dir, write_dir, kernel=ROOFLINE_KERNEL):
 def main():
     if len(sys.argv) >= 5 and sys.argv[1] == "table":
         print(json.dumps(table(sys.argv[2], sys.argv[3], sys.argv[4:]), indent=1))
+        return
+    if len(sys.argv) >= 4 and sys.argv[1] == "counters":
+        print(json.dumps(counters(sys.argv[2], sys.argv[3:]), indent=1))
         return
     if len(sys.argv) >= 4 and sys.argv[1] == "mfma":
         print(json.dumps(mfma(sys.argv[2], sys.argv[3:]), indent=1))
