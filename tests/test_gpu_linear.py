@@ -77,6 +77,8 @@ def test_single_linear_256_r8():
     (1, 100, 64, 1), (3, 257, 192, 5), (16, 300, 320, 8), (17, 129, 128, 16),
     (130, 200, 384, 33), (256, 512, 512, 64), (70, 1000, 640, 64), (129, 131, 64, 256),
     (200, 96, 1024, 2), (8, 136, 256, 100), (16, 72, 128, 256),
+    # few-token T projection with a partial pass of 9..15 tokens
+    (11, 260, 448, 24), (13, 520, 1024, 64),
     # from 1024 tokens the GEMM runs 512 x 128 tiles: ragged M, N and reductions there too
     (1030, 200, 384, 33), (1500, 1000, 640, 64), (2048, 131, 64, 256), (1100, 96, 1024, 2),
 ])
@@ -84,7 +86,7 @@ def test_ragged_shapes(M, N, K, r):
     run_case(M, N, K, r, 16.0, cfg=101)
 
 
-@pytest.mark.parametrize("M", [1, 16, 40])
+@pytest.mark.parametrize("M", [1, 13, 16, 40])
 def test_recompute_T_matches_saved_T(M):
     # M <= 16: the few-token projection runs in the forward and in the recompute
     got_saved = run_case(M, 200, 256, 16, 16.0, cfg=102, save_T=True)
