@@ -31,8 +31,8 @@ def pytest_collection_modifyitems(config, items):
 
 def pytest_terminal_summary(terminalreporter, exitstatus, config):
     """Margins of the floating-point parity checks (rel-L2 and max-abs / RMS
-    against their limits), printed and written to gpurun_out/parity_margins.json
-    (or $QLORA_PARITY_MARGINS)."""
+    against their limits), printed and written as JSON beside the run's other
+    outputs (or to $QLORA_PARITY_MARGINS)."""
     from tests import parity
     if not parity.MARGINS:
         return
