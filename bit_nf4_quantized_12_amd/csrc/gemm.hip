@@ -60,6 +60,29 @@ __device__ __forceinline__ BlockTable make_table(float chat, const Levels& lv) {
   return t;
 }
 
+// The table of a block shared by the 4 lanes of a quad (forward orientation
+// with 2 code words per thread: lanes 4r .. 4r + 3 hold the 4 parts of tile
+// row r, one block): lane p computes entries 4p .. 4p + 3 from its own levels
+// lq = q[4p .. 4p + 3] and the quad exchanges the byte planes by DPP. The
+// table is bit-identical to make_table's (the same products, packed and
+// permuted the same way, only computed by one lane each).
+__device__ __forceinline__ BlockTable make_table_quad(float chat, const float (&lq)[4]) {
+  const uint32_t pa = pack_bf16(__fmul_rn(lq[0], chat), __fmul_rn(lq[1], chat));
+  const uint32_t pb = pack_bf16(__fmul_rn(lq[2], chat), __fmul_rn(lq[3], chat));
+  const int lo = (int)perm(pb, pa, 0x06040200u), hi = (int)perm(pb, pa, 0x07050301u);
+  BlockTable t;
+  // quad_perm [j, j, j, j]: every lane of the quad reads lane j
+  t.L[0] = (uint32_t)__builtin_amdgcn_mov_dpp(lo, 0x00, 0xF, 0xF, false);
+  t.L[1] = (uint32_t)__builtin_amdgcn_mov_dpp(lo, 0x55, 0xF, 0xF, false);
+  t.L[2] = (uint32_t)__builtin_amdgcn_mov_dpp(lo, 0xAA, 0xF, 0xF, false);
+  t.L[3] = (uint32_t)__builtin_amdgcn_mov_dpp(lo, 0xFF, 0xF, 0xF, false);
+  t.H[0] = (uint32_t)__builtin_amdgcn_mov_dpp(hi, 0x00, 0xF, 0xF, false);
+  t.H[1] = (uint32_t)__builtin_amdgcn_mov_dpp(hi, 0x55, 0xF, 0xF, false);
+  t.H[2] = (uint32_t)__builtin_amdgcn_mov_dpp(hi, 0xAA, 0xF, 0xF, false);
+  t.H[3] = (uint32_t)__builtin_amdgcn_mov_dpp(hi, 0xFF, 0xF, 0xF, false);
+  return t;
+}
+
 // Look up the 8 codes of one word (element i in nibble i). Returns the bf16
 // of even elements in E (e0|e2<<16, e4|e6<<16) and odd ones in O (e1|e3<<16,
 // e5|e7<<16). Selector bytes: low 3 bits pick an entry inside a half table,
@@ -169,9 +192,9 @@ __device__ __forceinline__ void store_wword(uint32_t word, int q, const BlockTab
 }
 
 template <bool TW, int QW>
-__device__ __forceinline__ void store_wpart(const WPart<QW>& h, float chat, const Levels& lv,
+__device__ __forceinline__ void store_wpart(const WPart<QW>& h, float chat, const Levels& lv, const float (&lq)[4],
                                             uint16_t* __restrict__ dst, int tid) {
-  const BlockTable t = make_table(chat, lv);
+  const BlockTable t = (!TW && QW == 2) ? make_table_quad(chat, lq) : make_table(chat, lv);
 #pragma unroll
   for (int q = 0; q < QW; ++q) store_wword<TW, QW>(h.c[q], q, t, dst, tid);
 }
@@ -305,6 +328,15 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
     return h;
   };
 
+  // this lane's 4 levels for the quad-shared table (forward, 2 words per thread)
+  float lq[4];
+  {
+    const int qp = tid & 3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lq[i] = qp == 0 ? p.lv.q[i] : qp == 1 ? p.lv.q[4 + i] : qp == 2 ? p.lv.q[8 + i] : p.lv.q[12 + i];
+  }
+
   f32x4 acc[MI][4];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
@@ -314,7 +346,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
   // prologue: stage 0 complete, codes of the next step in flight
   load_x(kbeg, 0);
   WPart<QW> w0 = load_w(kbeg), w1;
-  store_wpart<TW, QW>(w0, wpart_chat<ABS>(w0), p.lv, sB, tid);
+  store_wpart<TW, QW>(w0, wpart_chat<ABS>(w0), p.lv, lq, sB, tid);
   w1 = load_w(kbeg + 1);
   __builtin_amdgcn_s_waitcnt(0);  // stage 0 LDS-DMA landed (vmcnt = lgkmcnt = 0)
   __syncthreads();
@@ -362,7 +394,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
     }
     // unpack the next weight tile into the other stage (free since the last
     // barrier); steps past the end unpack a clamped block into an unused stage
-    store_wpart<TW, QW>(cur, wpart_chat<ABS>(cur), p.lv, sB + (st ^ 1) * BN * 64, tid);
+    store_wpart<TW, QW>(cur, wpart_chat<ABS>(cur), p.lv, lq, sB + (st ^ 1) * BN * 64, tid);
     __builtin_amdgcn_s_waitcnt(kStepWait);  // this step's LDS-DMA and LDS writes are complete
     __builtin_amdgcn_s_barrier();
   };
