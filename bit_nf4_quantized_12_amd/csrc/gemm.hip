@@ -130,6 +130,15 @@ __device__ __forceinline__ uint4 load_row8(const uint16_t* __restrict__ base, in
 // XOR-swizzled per row (lds_swz).
 __device__ __forceinline__ int swz(int R) { return lds_swz(R); }
 __device__ __forceinline__ int tile_off(int R, int c) { return R * 64 + 8 * (c ^ swz(R)); }
+// The input gradient's weight tiles take the same swizzle with the chunk
+// also XORed by 2 ((R >> 4) & 3): a fragment read covers 16 consecutive rows
+// (one group, a constant extra XOR: still conflict free), while its unpack
+// has the 4 lanes of a quad write one reduction position of 4 rows 16 apart,
+// which the extra XOR sends to different banks.
+template <bool TW>
+__device__ __forceinline__ int bswz(int R) { return TW ? lds_swz(R) ^ (((R >> 4) & 3) << 1) : lds_swz(R); }
+template <bool TW>
+__device__ __forceinline__ int btile_off(int R, int c) { return R * 64 + 8 * (c ^ bswz<TW>(R)); }
 
 // The QW code words (8 QW codes of one block) a thread unpacks in a step,
 // and their block constant.
@@ -151,7 +160,10 @@ __device__ __forceinline__ float wpart_chat(const WPart<QW>& h) {
 
 // Thread -> weight codes of a step (QW words = 8 QW codes; TPR = 8 / QW
 // threads share a block). Forward: thread t owns tile row t / TPR (weight
-// row n0 + t / TPR), part t % TPR of the step's block. Input gradient: lane
+// row n0 + t / TPR), part t % TPR of the step's block. Input gradient with 2
+// words a thread: the 4 lanes of a quad share one block, weight row
+// k0 + (l >> 2) + 16 (w & 3), columns n0 + 64 (w >> 2) + 16 (l & 3) .. (a
+// quad reads 32 contiguous bytes and builds one table); with 4 words: lane
 // l owns weight row k0 + l, wave w the weight columns n0 + 8 QW w ..
 template <bool TW, int QW>
 __device__ __forceinline__ void wlane(int tid, int n0, int64_t& row, int64_t& col) {
@@ -160,6 +172,9 @@ __device__ __forceinline__ void wlane(int tid, int n0, int64_t& row, int64_t& co
   if (!TW) {
     row = n0 + tid / TPR;
     col = 8 * QW * (tid % TPR);
+  } else if (QW == 2) {
+    row = (l >> 2) + 16 * (w & 3);
+    col = n0 + 64 * (w >> 2) + 16 * (l & 3);
   } else {
     row = l;
     col = n0 + 8 * QW * w;
@@ -176,25 +191,26 @@ __device__ __forceinline__ void store_wword(uint32_t word, int q, const BlockTab
     // tile row tid / TPR, reduction chunk QW (tid % TPR) + q
     uint32_t o[4];
     lookup8(word, t, o);
-    *reinterpret_cast<uint4*>(dst + tile_off(tid / TPR, QW * (tid % TPR) + q)) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(dst + btile_off<TW>(tid / TPR, QW * (tid % TPR) + q)) = make_uint4(o[0], o[1], o[2], o[3]);
   } else {
-    // element e of the word is W~[k0 + l][n0 + 8 QW w + 8 q + e]: tile row
-    // 8 QW w + 8 q + e, reduction position l
+    // element e of the word is W~[k0 + k][n0 + r0 + e] (wlane's row k and
+    // column r0 + e of the tile): tile row r0 + e, reduction position k
     const int w = tid >> 6, l = tid & 63;
     uint32_t E[2], O[2];
     lookup8_split(word, t, E, O);
-    const int r0 = 8 * QW * w + 8 * q;
+    const int r0 = QW == 2 ? 64 * (w >> 2) + 16 * (l & 3) + 8 * q : 8 * QW * w + 8 * q;
+    const int k = QW == 2 ? (l >> 2) + 16 * (w & 3) : l;
     const uint16_t v[8] = {(uint16_t)E[0], (uint16_t)O[0], (uint16_t)(E[0] >> 16), (uint16_t)(O[0] >> 16),
                            (uint16_t)E[1], (uint16_t)O[1], (uint16_t)(E[1] >> 16), (uint16_t)(O[1] >> 16)};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dst[tile_off(r0 + e, l >> 3) + (l & 7)] = v[e];
+    for (int e = 0; e < 8; ++e) dst[btile_off<TW>(r0 + e, k >> 3) + (k & 7)] = v[e];
   }
 }
 
 template <bool TW, int QW>
 __device__ __forceinline__ void store_wpart(const WPart<QW>& h, float chat, const Levels& lv, const float (&lq)[4],
                                             uint16_t* __restrict__ dst, int tid) {
-  const BlockTable t = (!TW && QW == 2) ? make_table_quad(chat, lq) : make_table(chat, lv);
+  const BlockTable t = QW == 2 ? make_table_quad(chat, lq) : make_table(chat, lv);
 #pragma unroll
   for (int q = 0; q < QW; ++q) store_wword<TW, QW>(h.c[q], q, t, dst, tid);
 }
@@ -328,7 +344,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
     return h;
   };
 
-  // this lane's 4 levels for the quad-shared table (forward, 2 words per thread)
+  // this lane's 4 levels for the quad-shared table (2 words per thread)
   float lq[4];
   {
     const int qp = tid & 3;
@@ -384,7 +400,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
       const int ck = kk ? ck1 : ck0;
       bf16x8 b[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = lds_load8(reinterpret_cast<const __bf16*>(b_s + (brow + 16 * j) * 64 + ck));
+      for (int j = 0; j < 4; ++j) b[j] = lds_load8(reinterpret_cast<const __bf16*>(b_s + (brow + 16 * j) * 64 + (TW ? ck ^ (16 * j) : ck)));
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         const bf16x8 a = lds_load8(reinterpret_cast<const __bf16*>(a_s + (arow + 16 * i) * 64 + ck));
@@ -432,7 +448,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int j = 0; j < BN / 64; ++j) {
         const int R = (BN / 8) * wu + 8 * j + (l >> 3);
-        const int c = (l & 7) ^ swz(R);
+        const int c = (l & 7) ^ bswz<TW>(R);
         const int rb = min(n0 + R, p.Nout - 1);
         __builtin_amdgcn_global_load_lds((gbl_void_t*)(p.lora_r + (int64_t)rb * p.rp + kr + 8 * c),
                                          (lds_void_t*)(sB + ((BN / 8) * wu + 8 * j) * 64), 16, 0, 0);
@@ -444,7 +460,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
         const int ck = kk ? ck1 : ck0;
         bf16x8 b[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = lds_load8(reinterpret_cast<const __bf16*>(sB + (brow + 16 * j) * 64 + ck));
+        for (int j = 0; j < 4; ++j) b[j] = lds_load8(reinterpret_cast<const __bf16*>(sB + (brow + 16 * j) * 64 + (TW ? ck ^ (16 * j) : ck)));
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
           const bf16x8 a = lds_load8(reinterpret_cast<const __bf16*>(sA + (arow + 16 * i) * 64 + ck));
