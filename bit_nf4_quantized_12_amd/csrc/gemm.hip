@@ -162,9 +162,11 @@ __device__ __forceinline__ float wpart_chat(const WPart<QW>& h) {
 // threads share a block). Forward: thread t owns tile row t / TPR (weight
 // row n0 + t / TPR), part t % TPR of the step's block. Input gradient with 2
 // words a thread: the 4 lanes of a quad share one block, weight row
-// k0 + (l >> 2) + 16 (w & 3), columns n0 + 64 (w >> 2) + 16 (l & 3) .. (a
-// quad reads 32 contiguous bytes and builds one table); with 4 words: lane
-// l owns weight row k0 + l, wave w the weight columns n0 + 8 QW w ..
+// k0 + 2 ((l >> 2) & 7) + (l >> 5) + 16 (w & 3), columns
+// n0 + 64 (w >> 2) + 16 (l & 3) .. (a quad reads 32 contiguous bytes and
+// builds one table; lanes l and l + 32 hold adjacent rows of the same
+// columns); with 4 words: lane l owns weight row k0 + l, wave w the weight
+// columns n0 + 8 QW w ..
 template <bool TW, int QW>
 __device__ __forceinline__ void wlane(int tid, int n0, int64_t& row, int64_t& col) {
   constexpr int TPR = 8 / QW;
@@ -173,7 +175,7 @@ __device__ __forceinline__ void wlane(int tid, int n0, int64_t& row, int64_t& co
     row = n0 + tid / TPR;
     col = 8 * QW * (tid % TPR);
   } else if (QW == 2) {
-    row = (l >> 2) + 16 * (w & 3);
+    row = 2 * ((l >> 2) & 7) + (l >> 5) + 16 * (w & 3);
     col = n0 + 64 * (w >> 2) + 16 * (l & 3);
   } else {
     row = l;
@@ -198,8 +200,8 @@ __device__ __forceinline__ void store_wword(uint32_t word, int q, const BlockTab
     const int w = tid >> 6, l = tid & 63;
     uint32_t E[2], O[2];
     lookup8_split(word, t, E, O);
-    const int r0 = QW == 2 ? 64 * (w >> 2) + 16 * (l & 3) + 8 * q : 8 * QW * w + 8 * q;
-    const int k = QW == 2 ? (l >> 2) + 16 * (w & 3) : l;
+    const int r0 = 8 * QW * w + 8 * q;
+    const int k = l;
     const uint16_t v[8] = {(uint16_t)E[0], (uint16_t)O[0], (uint16_t)(E[0] >> 16), (uint16_t)(O[0] >> 16),
                            (uint16_t)E[1], (uint16_t)O[1], (uint16_t)(E[1] >> 16), (uint16_t)(O[1] >> 16)};
 #pragma unroll
@@ -207,12 +209,45 @@ __device__ __forceinline__ void store_wword(uint32_t word, int q, const BlockTab
   }
 }
 
+// Input gradient, 2 words a thread: lanes l and l + 32 hold reduction
+// positions k and k + 1 (k even) of the same 16 columns. One lane swap per
+// packed pair leaves each lane both positions of 8 columns (lanes below 32:
+// the first 8, the others: the last 8), stored as bf16 pairs k | k + 1.
+__device__ __forceinline__ void store_tw2(const uint32_t (&c)[2], const BlockTable& t, uint16_t* __restrict__ dst,
+                                          int tid) {
+  const int w = tid >> 6, l = tid & 63;
+  uint32_t E0[2], O0[2], E1[2], O1[2];
+  lookup8_split(c[0], t, E0, O0);
+  lookup8_split(c[1], t, E1, O1);
+  const uint32_t a[4] = {E0[0], O0[0], E0[1], O0[1]};
+  const uint32_t b[4] = {E1[0], O1[0], E1[1], O1[1]};
+  uint32_t X[4], Y[4];  // split pairs of positions k (X) and k + 1 (Y)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(a[i], b[i], false, false);
+    X[i] = r[0];
+    Y[i] = r[1];
+  }
+  const int k = 2 * ((l >> 2) & 7) + 16 * (w & 3);
+  const int r0 = 64 * (w >> 2) + 16 * (l & 3) + 8 * (l >> 5);
+  const uint32_t v[8] = {perm(Y[0], X[0], 0x05040100u), perm(Y[1], X[1], 0x05040100u),
+                         perm(Y[0], X[0], 0x07060302u), perm(Y[1], X[1], 0x07060302u),
+                         perm(Y[2], X[2], 0x05040100u), perm(Y[3], X[3], 0x05040100u),
+                         perm(Y[2], X[2], 0x07060302u), perm(Y[3], X[3], 0x07060302u)};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) *reinterpret_cast<uint32_t*>(dst + btile_off<true>(r0 + e, k >> 3) + (k & 7)) = v[e];
+}
+
 template <bool TW, int QW>
 __device__ __forceinline__ void store_wpart(const WPart<QW>& h, float chat, const Levels& lv, const float (&lq)[4],
                                             uint16_t* __restrict__ dst, int tid) {
   const BlockTable t = QW == 2 ? make_table_quad(chat, lq) : make_table(chat, lv);
+  if constexpr (TW && QW == 2) {
+    store_tw2(h.c, t, dst, tid);
+  } else {
 #pragma unroll
-  for (int q = 0; q < QW; ++q) store_wword<TW, QW>(h.c[q], q, t, dst, tid);
+    for (int q = 0; q < QW; ++q) store_wword<TW, QW>(h.c[q], q, t, dst, tid);
+  }
 }
 
 // QW code words at codes + (e >> 1) (e a multiple of 8 QW).
