@@ -253,7 +253,7 @@ __device__ __forceinline__ void store_wpart(const WPart<QW>& h, float chat, cons
 // QW code words at codes + (e >> 1) (e a multiple of 8 QW).
 template <int QW>
 __device__ __forceinline__ void load_words(const uint8_t* __restrict__ codes, int64_t e, uint32_t (&c)[QW]) {
-  if (QW == 4) {
+  if constexpr (QW == 4) {
     const uint4 v = *reinterpret_cast<const uint4*>(codes + (e >> 1));
     c[0] = v.x; c[1] = v.y; c[2] = v.z; c[3] = v.w;
   } else {
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
   // (i & 7) ^ swz(row). Rows past the end are clamped (they only feed
   // unstored outputs); steps past the end reload the last step (prefetch
   // overrun, never used). Lane byte offsets are fixed; the step moves a
-  // uniform base.
+  // uniform base. Instructions jb .. je - 1 of the step are issued.
   uint32_t xoff[XJ];
 #pragma unroll
   for (int j = 0; j < XJ; ++j) {
@@ -317,12 +317,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
     const int row = min(m0 + R, p.M - 1);
     xoff[j] = (uint32_t)(row * p.Kred + 8 * ((l & 7) ^ swz(R))) * 2u;
   }
-  auto load_x = [&](int kt, int st) {
+  auto load_x = [&](int kt, int st, int jb, int je) {
     if (VEC) {
       const int ke = min(kt, nk - 1);
       const char* base = reinterpret_cast<const char*>(p.act) + (size_t)ke * (BK * 2);
 #pragma unroll
-      for (int j = 0; j < XJ; ++j)
+      for (int j = jb; j < je; ++j)
         __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + xoff[j]),
                                          (lds_void_t*)(sA + st * BM * 64 + ((BM / 8) * wu + 8 * j) * 64), 16, 0, 0);
     } else {
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // prologue: stage 0 complete, codes of the next step in flight
-  load_x(kbeg, 0);
+  load_x(kbeg, 0, 0, XJ);
   WPart<QW> w0 = load_w(kbeg), w1;
   store_wpart<TW, QW>(w0, wpart_chat<ABS>(w0), p.lv, lq, sB, tid);
   w1 = load_w(kbeg + 1);
@@ -420,10 +420,17 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
   // The large tiles have no registers to spare for that (it spills) and wait
   // for everything at the end of each step.
   constexpr bool KEEP = WM == 32 && VEC;
+  // 512-row tiles issue the next step's activation DMA in pieces between the
+  // first half-step's MFMA groups (one instruction ahead of each fragment
+  // row forward, two ahead of every second row for the input gradient):
+  // measured 2-4 % faster than one burst of 8 ahead of all the MFMAs.
+  constexpr bool SPREAD = VEC && !KEEP && BM == 512;
+  constexpr int DPI = TW ? 2 : 1;
+  static_assert(!SPREAD || XJ == MI, "one DMA instruction per fragment row");
   constexpr int NCODE = ABS ? 2 : 3;  // code words + block constant(s)
   constexpr int kStepWait = KEEP ? (NCODE | (7 << 4)) : 0;  // vmcnt(NCODE), expcnt any, lgkmcnt(0)
   auto step = [&](int kt, int st, WPart<QW>& next, const WPart<QW>& cur) {
-    load_x(kt + 1, st ^ 1);
+    if (!SPREAD) load_x(kt + 1, st ^ 1, 0, XJ);
     if (KEEP) __builtin_amdgcn_sched_barrier(0);
     next = load_w(kt + 2);
     if (KEEP) __builtin_amdgcn_sched_barrier(0);
@@ -438,6 +445,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
       for (int j = 0; j < 4; ++j) b[j] = lds_load8(reinterpret_cast<const __bf16*>(b_s + (brow + 16 * j) * 64 + (TW ? ck ^ (16 * j) : ck)));
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
+        if (SPREAD && kk == 0 && i % DPI == 0) load_x(kt + 1, st ^ 1, i, i + DPI);
         const bf16x8 a = lds_load8(reinterpret_cast<const __bf16*>(a_s + (arow + 16 * i) * 64 + ck));
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a, b[j], acc[i][j]);
