@@ -450,11 +450,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
   // for everything at the end of each step.
   constexpr bool KEEP = WM == 32 && VEC;
   // 512-row tiles issue the next step's activation DMA in pieces between the
-  // first half-step's MFMA groups (one instruction ahead of each fragment
-  // row forward, two ahead of every second row for the input gradient):
-  // measured 2-4 % faster than one burst of 8 ahead of all the MFMAs.
+  // first half-step's MFMA groups (one instruction behind the MFMAs of each
+  // fragment row): measured 3-5 % faster than one burst of 8 ahead of all
+  // the MFMAs, which stalls the wave before its first MFMA while the vector
+  // memory path is still busy.
   constexpr bool SPREAD = VEC && !KEEP && BM == 512;
-  constexpr int DPI = TW ? 2 : 1;
   static_assert(!SPREAD || XJ == MI, "one DMA instruction per fragment row");
   constexpr int NCODE = ABS ? 2 : 3;  // code words + block constant(s)
   constexpr int kStepWait = KEEP ? (NCODE | (7 << 4)) : 0;  // vmcnt(NCODE), expcnt any, lgkmcnt(0)
@@ -474,10 +474,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
       for (int j = 0; j < 4; ++j) b[j] = lds_load8(reinterpret_cast<const __bf16*>(b_s + (brow + 16 * j) * 64 + (TW ? ck ^ (16 * j) : ck)));
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
-        if (SPREAD && kk == 0 && i % DPI == 0) load_x(kt + 1, st ^ 1, i, i + DPI);
         const bf16x8 a = lds_load8(reinterpret_cast<const __bf16*>(a_s + (arow + 16 * i) * 64 + ck));
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a, b[j], acc[i][j]);
+        if (SPREAD && kk == 0) load_x(kt + 1, st ^ 1, i, i + 1);
       }
     }
     // unpack the next weight tile into the other stage (free since the last
