@@ -19,13 +19,17 @@
 // holds two stages of the activation tile and of the weight tile (bf16,
 // 128 or 160 KB in all, 16-byte chunks XOR-swizzled per row so MFMA operand
 // reads are conflict free). The activation tile is streamed global -> LDS
-// by LDS-DMA (global_load_lds_dwordx4); no registers involved.
+// by LDS-DMA, no registers involved: 512-row tiles issue it as buffer loads
+// spread over the first half-step's MFMAs, the others as global loads at
+// the top of the step.
 //
 // Weight tiles are unpacked in registers: each thread owns BN / 8 codes of
-// one block per step (half or a quarter of it), builds the block's 16-entry
-// table of bf16(q[c] * c^) (16 multiplies, 8 conversions, 8 byte shuffles)
-// and maps every code through it with v_perm byte selects -- no LDS lookups,
-// exact W~. Codes are fetched two steps ahead, activations one step ahead.
+// one block per step (a quarter or half of it), the block's 16-entry table
+// of bf16(q[c] * c^) is built by the lanes that share the block (with a
+// quarter each, every lane of a quad computes 4 entries and DPP broadcasts
+// them; with a half, each lane computes all 16), and every code is mapped
+// through it with v_perm byte selects -- no LDS lookups, exact W~. Codes are
+// fetched two steps ahead, activations one step ahead.
 //
 // Workgroups are ordered so that each XCD (workgroup id mod 8) owns a
 // contiguous band of output tiles: the activation rows and weight columns
