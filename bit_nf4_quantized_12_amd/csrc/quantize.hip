@@ -84,6 +84,85 @@ __device__ __forceinline__ uint32_t e4m3_code(float rho) {
   return (uint32_t)__builtin_rintf(rho * 512.0f);  // subnormal: m * 2^-9, m in 0..8
 }
 
+// Codes of this lane's 8 chunks of 8 weights (chunk j: elements
+// gbase + 4096 wave + 512 j + 8 lane ..), their block maxima (bmax[j], the
+// same on the 8 lanes of a block) and the running group max. FULL: the whole
+// group lies inside the tensor.
+template <bool FULL>
+__device__ __forceinline__ void quant_rows(const uint16_t* __restrict__ w, uint8_t* __restrict__ codes, int64_t n,
+                                           int64_t gbase, int wave, int lane, const float2* __restrict__ tab,
+                                           float scale, float (&bmax)[8], float& gmax) {
+  const int64_t e0 = gbase + wave * 4096 + lane * 8;
+  uint4 v[8];
+  if constexpr (FULL) {
+    // all 32 KB of the group in flight at once
+    const u32x4* wp = reinterpret_cast<const u32x4*>(w + e0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const u32x4 t = __builtin_nontemporal_load(wp + 64 * j);
+      v[j] = make_uint4(t[0], t[1], t[2], t[3]);
+    }
+  }
+  uint32_t* cp = reinterpret_cast<uint32_t*>(codes + (e0 >> 1));
+
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if constexpr (!FULL) {
+      // a tensor's last group: element loads, one chunk at a time (this path
+      // runs once per tensor; loading it all up front would set the
+      // kernel's register budget, and so its occupancy, for every group)
+      const int64_t e = e0 + j * 512;
+      uint32_t h[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[i] = (e + i < n) ? w[e + i] : 0u;
+      v[j] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+    }
+    float f[8];
+    f[0] = bf16lo(v[j].x); f[1] = bf16hi(v[j].x);
+    f[2] = bf16lo(v[j].y); f[3] = bf16hi(v[j].y);
+    f[4] = bf16lo(v[j].z); f[5] = bf16hi(v[j].z);
+    f[6] = bf16lo(v[j].w); f[7] = bf16hi(v[j].w);
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+    m = dpp_max8(m);
+    bmax[j] = m;
+    gmax = fmaxf(gmax, m);
+
+    // an all-zero block is divided by 1: its weights are +-0 and map to the
+    // exact zero like any x = 0
+    const float md = m > 0.0f ? m : 1.0f;
+    const bool fast = md >= 0x1p-100f && md <= 0x1p100f;
+    const float r = rcp_bf16(md);  // used by the lanes with `fast` only
+    uint32_t word = 0;
+    if (__all(fast)) {
+      // every block of the wave in range (wave-uniform branch): the
+      // straight-line correctly rounded quotient
+#pragma unroll
+      for (int i = 0; i < 8; ++i) word |= nearest_code(div_block(f[i], md, r, true), tab, scale) << (4 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) word |= nearest_code(div_block(f[i], md, r, fast), tab, scale) << (4 * i);
+    }
+    if constexpr (FULL) {
+      __builtin_nontemporal_store(word, cp + 64 * j);
+    } else {
+      const int64_t e = e0 + j * 512;
+      if (e + 8 <= n) {
+        __builtin_nontemporal_store(word, cp + 64 * j);
+      } else if (e < n) {
+        // short tail: elements past n get code 0, bytes past ceil(n/2) are not written
+        const int valid = (int)(n - e);
+        const uint32_t keep = (1u << (4 * valid)) - 1u;
+        word &= keep;
+        const int bytes = (valid + 1) >> 1;
+        for (int b = 0; b < bytes; ++b) codes[(e >> 1) + b] = (uint8_t)(word >> (8 * b));
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the chunks apart (registers)
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void quantize_kernel(QuantBatch bt, QuantTable qt) {
   __shared__ float2 s_tab[kQuantCells + 1];
   __shared__ float s_wmax[4];
@@ -108,67 +187,16 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantBatch bt, QuantTable
   const int64_t nb = (n + kBlock - 1) / kBlock;
   const bool full = gbase + kGroup <= n;
 
-  uint4 v[8];
-  if (full) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t e = gbase + wave * 4096 + j * 512 + lane * 8;
-      const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w + e));
-      v[j] = make_uint4(t[0], t[1], t[2], t[3]);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t e = gbase + wave * 4096 + j * 512 + lane * 8;
-      uint32_t h[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) h[i] = (e + i < n) ? w[e + i] : 0u;
-      v[j] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-    }
-  }
-
   float bmax[8];
   float gmax = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int64_t e = gbase + wave * 4096 + j * 512 + lane * 8;
-    float f[8];
-    f[0] = bf16lo(v[j].x); f[1] = bf16hi(v[j].x);
-    f[2] = bf16lo(v[j].y); f[3] = bf16hi(v[j].y);
-    f[4] = bf16lo(v[j].z); f[5] = bf16hi(v[j].z);
-    f[6] = bf16lo(v[j].w); f[7] = bf16hi(v[j].w);
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
-    m = dpp_max8(m);
-    bmax[j] = m;
-    gmax = fmaxf(gmax, m);
-
-    // an all-zero block is divided by 1: its weights are +-0 and map to the
-    // exact zero like any x = 0
-    const float md = m > 0.0f ? m : 1.0f;
-    const bool fast = md >= 0x1p-100f && md <= 0x1p100f;
-    const float r = rcp_bf16(md);  // used by the lanes with `fast` only
-    uint32_t word = 0;
-    if (__all(fast)) {
-      // every block of the wave in range (wave-uniform branch): the
-      // straight-line correctly rounded quotient
-#pragma unroll
-      for (int i = 0; i < 8; ++i) word |= nearest_code(div_block(f[i], md, r, true), s_tab, qt.scale) << (4 * i);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) word |= nearest_code(div_block(f[i], md, r, fast), s_tab, qt.scale) << (4 * i);
-    }
-    if (full || e + 8 <= n) {
-      __builtin_nontemporal_store(word, reinterpret_cast<uint32_t*>(codes + (e >> 1)));
-    } else if (e < n) {
-      // short tail: elements past n get code 0, bytes past ceil(n/2) are not written
-      const int valid = (int)(n - e);
-      const uint32_t keep = valid >= 8 ? 0xFFFFFFFFu : ((1u << (4 * valid)) - 1u);
-      word &= keep;
-      const int bytes = (valid + 1) >> 1;
-      for (int b = 0; b < bytes; ++b) codes[(e >> 1) + b] = (uint8_t)(word >> (8 * b));
-    }
+  // A full group (all but a tensor's last) takes the straight path: no
+  // bounds checks, and every load and store at a constant offset from one
+  // per-lane base (the checks and 64-bit index arithmetic of the general
+  // path cost about as many instructions as the search itself).
+  if (full) {
+    quant_rows<true>(w, codes, n, gbase, wave, lane, s_tab, qt.scale, bmax, gmax);
+  } else {
+    quant_rows<false>(w, codes, n, gbase, wave, lane, s_tab, qt.scale, bmax, gmax);
   }
 
   if (absmax_out) {
