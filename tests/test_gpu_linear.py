@@ -81,6 +81,9 @@ def test_single_linear_256_r8():
     (11, 260, 448, 24), (13, 520, 1024, 64),
     # from 1024 tokens the GEMM runs 512 x 128 tiles: ragged M, N and reductions there too
     (1030, 200, 384, 33), (1500, 1000, 640, 64), (2048, 131, 64, 256), (1100, 96, 1024, 2),
+    # input gradient whose last 128-column tile is half past K (quads of lanes whose block lies
+    # past the end share a clamped block), with 512 x 128 and 128 x 128 tiles
+    (1040, 300, 192, 16), (200, 448, 192, 8),
 ])
 def test_ragged_shapes(M, N, K, r):
     run_case(M, N, K, r, 16.0, cfg=101)
