@@ -52,7 +52,7 @@ def _case(M, g, ns, K, r, seed, cb="nf4", dq=True, save_T=True, need_dX=True):
 
 @pytest.mark.parametrize("M,g,ns,K,r", [
     (16, 3, 256, 256, 64),      # few-token forward path
-    (300, 3, 256, 384, 64),     # ragged rows, 256 x 256 tiles
+    (300, 3, 256, 384, 64),     # ragged rows, 128 x 128 tiles
     (1100, 2, 512, 256, 128),   # 512 x 128 tiles, two 64-column blocks per segment
     (1024, 4, 256, 512, 64),
     (8, 2, 256, 128, 192),

@@ -84,6 +84,8 @@ def test_single_linear_256_r8():
     # input gradient whose last 128-column tile is half past K (quads of lanes whose block lies
     # past the end share a clamped block), with 512 x 128 and 128 x 128 tiles
     (1040, 300, 192, 16), (200, 448, 192, 8),
+    # 256 x 256 tiles (under 1024 tokens, at least 192 tiles): forward, then input gradient
+    (600, 16640, 256, 16), (600, 256, 16640, 16),
 ])
 def test_ragged_shapes(M, N, K, r):
     run_case(M, N, K, r, 16.0, cfg=101)
