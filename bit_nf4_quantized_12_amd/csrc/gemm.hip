@@ -283,6 +283,11 @@ struct BufRsrc {
 __device__ __forceinline__ void dma16(const BufRsrc& r, uint16_t* lds, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r.rs, (lds_void_t*)lds, 16, voff, soff, 0, 0);
 }
+// One dword through the same resource: brings its cache line into L2 (the
+// value itself is not needed).
+__device__ __forceinline__ uint32_t touch4(const BufRsrc& r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r.rs, (int)voff, (int)soff, 0);
+}
 
 template <int BM, int BN, bool TW, bool LORA, bool VEC, bool ABS>
 __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
@@ -367,6 +372,27 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
         *reinterpret_cast<uint4*>(&sA[st * BM * 64 + tile_off(id >> 3, id & 7)]) = v;
       }
     }
+  };
+
+  // L2 prefetch of the activation tile PFD steps ahead (512-row tiles). The
+  // workgroups an XCD runs at once stream the same activation band (the tile
+  // order gives them consecutive output-column tiles), so each touches 1/32
+  // of the band's lines -- 16 rows, two 64-byte halves of each row's
+  // 128-byte step segment, 2 rows per wave (lane l takes address l & 3, so
+  // the instruction needs no branch) -- and the band's next tiles are in
+  // that XCD's L2 before the DMA asks for them. Without it the DMA of a band
+  // larger than the Infinity Cache waits on HBM at the end of the step. The
+  // loaded dwords are discarded.
+  constexpr bool PF = VEC && BM == 512;
+  constexpr int PFD = 3;
+  uint32_t pfoff = 0, pf = 0;
+  if (PF) {
+    const int R = 16 * ((t % gn) & 31) + 2 * wu + ((l >> 1) & 1);
+    const int row = min(m0 + R, p.M - 1);
+    pfoff = (uint32_t)((row - xrow0) * p.Kred) * 2u + (uint32_t)(l & 1) * 64u;
+  }
+  auto prefetch_x = [&](int kt) {
+    if (PF) pf = touch4(xrs, pfoff, (uint32_t)min(kt, nk - 1) * (BK * 2));
   };
 
   // ---- weight codes of step kt ------------------------------------------------------
@@ -466,6 +492,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
   constexpr int NCODE = ABS ? 2 : 3;  // code words + block constant(s)
   constexpr int kStepWait = KEEP ? (NCODE | (7 << 4)) : 0;  // vmcnt(NCODE), expcnt any, lgkmcnt(0)
   auto step = [&](int kt, int st, WPart<QW>& next, const WPart<QW>& cur) {
+    prefetch_x(kt + PFD);
     if (!SPREAD) load_x(kt + 1, st ^ 1, 0, XJ);
     if (KEEP) __builtin_amdgcn_sched_barrier(0);
     next = load_w(kt + 2);
@@ -492,6 +519,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
     store_wpart<TW, QW>(cur, wpart_chat<ABS>(cur), p.lv, lq, sB + (st ^ 1) * BN * 64, tid);
     __builtin_amdgcn_s_waitcnt(kStepWait);  // this step's LDS-DMA and LDS writes are complete
     __builtin_amdgcn_s_barrier();
+    // the prefetch register stays allocated until its load has completed
+    // (reusing it earlier would make the compiler wait for that load)
+    if (PF) asm volatile("" ::"v"(pf));
   };
   if (KEEP) {
     int kt = kbeg;

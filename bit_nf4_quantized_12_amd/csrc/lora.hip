@@ -118,17 +118,56 @@ typedef __attribute__((address_space(1))) void gbl_void_t;
 constexpr int PJ_STAGES = 4;
 __device__ __forceinline__ int pj_swz(int R) { return lds_swz(R); }
 
+// Workgroup -> (x, y, z) of a gx x gy x gz grid launched as 8 ceil(gx gy gz
+// / 8) workgroups in one dimension. When the z blocks read the same input
+// tile (zshare: the rank blocks of one row tile), workgroup g, which runs on
+// XCD g % 8, takes item g / 8 of XCD i's contiguous range [i per,
+// (i + 1) per) of the order with z fastest, then x, then y: the blocks that
+// share a tile run at the same time on one XCD and fetch it from HBM once,
+// through that XCD's L2 (as a 3-D grid they ran in separate rounds, each
+// reading it again). Otherwise the order is the 3-D grid's own (x fastest,
+// then y, then z, dealt round robin over the XCDs), which streams
+// neighbouring column tiles together and measured faster there.
+struct Wg3 {
+  int x, y, z;
+  bool ok;
+};
+__device__ __forceinline__ Wg3 xcd_wg3(int gx, int gy, int gz, bool zshare) {
+  const int total = gx * gy * gz;
+  Wg3 r;
+  if (zshare && gz > 1) {
+    const int per = (total + 7) / 8;
+    const int u = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+    r.ok = u < total;
+    r.z = u % gz;
+    const int rest = u / gz;
+    r.x = rest % gx;
+    r.y = rest / gx;
+  } else {
+    const int u = (int)blockIdx.x;
+    r.ok = u < total;
+    r.x = u % gx;
+    const int rest = u / gx;
+    r.y = rest % gy;
+    r.z = rest / gy;
+  }
+  return r;
+}
+inline unsigned xcd_grid(int gx, int gy, int gz) { return 8u * (unsigned)((gx * gy * gz + 7) / 8); }
+
 __global__ __launch_bounds__(256) void proj_stream_kernel(const uint16_t* __restrict__ L, int64_t ldL,
                                                            int64_t segL, const uint16_t* __restrict__ R,
                                                            int64_t ldR, int64_t segR, int zper, int M,
                                                            int Kr, int r_seg, int rp_total, int kslice,
-                                                           float* __restrict__ part) {
+                                                           int nsplit, float* __restrict__ part) {
   __shared__ __align__(16) uint16_t sm[PJ_STAGES][2][64 * 64];
+  const Wg3 wg = xcd_wg3((M + 63) / 64, nsplit, rp_total / 64, segL == 0);
+  if (!wg.ok) return;
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int m0 = blockIdx.x * 64;
-  const int ks = blockIdx.y;
-  const int z = blockIdx.z;
+  const int m0 = wg.x * 64;
+  const int ks = wg.y;
+  const int z = wg.z;
   const int kbeg = ks * kslice;
   const int nsteps = max(0, min(Kr - kbeg, kslice)) / 64;
   const int zs = z / zper, zb = z - zs * zper;
@@ -430,14 +469,16 @@ __global__ __launch_bounds__(512) void grad_tr_kernel(const uint16_t* __restrict
                                                        const uint16_t* __restrict__ Pl,
                                                        const uint16_t* __restrict__ Q, int M,
                                                        int Mp, int C, int rp, int mchunk, int segC,
-                                                       int rseg, float* __restrict__ part) {
+                                                       int rseg, int nsplit, float* __restrict__ part) {
   extern __shared__ __align__(16) uint16_t gsm[];
+  const Wg3 wg = xcd_wg3((C + 127) / 128, nsplit, rseg / 64, true);
+  if (!wg.ok) return;
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int jb = w & 3, ch = w >> 2;
-  const int cbase = blockIdx.x * 128;
-  const int s = blockIdx.y;
-  const int jc = blockIdx.z;
+  const int cbase = wg.x * 128;
+  const int s = wg.y;
+  const int jc = wg.z;
   const int mbeg = s * mchunk;
   const int nsteps = max(0, min(Mp - mbeg, mchunk)) / 64;
 
@@ -638,9 +679,9 @@ hipError_t launch_proj_seg(const uint16_t* L, int64_t ldL, int64_t segL, const u
                            int64_t segR, int zper, int M, int Kr, int r_seg, int rp_total, int nsplit, float* part,
                            hipStream_t s) {
   const int kslice = ((Kr + nsplit - 1) / nsplit + 63) / 64 * 64;
-  dim3 grid((M + 63) / 64, nsplit, rp_total / 64);
+  const dim3 grid(xcd_grid((M + 63) / 64, nsplit, rp_total / 64));
   hipLaunchKernelGGL(proj_stream_kernel, grid, dim3(256), 0, s, L, ldL, segL, R, ldR, segR, zper, M, Kr, r_seg,
-                     rp_total, kslice, part);
+                     rp_total, kslice, nsplit, part);
   return hipGetLastError();
 }
 
@@ -691,13 +732,13 @@ hipError_t launch_grad_tr(const uint16_t* Ph, const uint16_t* Pl, const uint16_t
   if (e == hipSuccess) e = ensure_lds(reinterpret_cast<const void*>(&grad_tr_kernel<true>), (int)smem, lds_ok[1]);
   if (e != hipSuccess) return e;
   const int mchunk = ((Mp + nsplit - 1) / nsplit + 63) / 64 * 64;
-  dim3 grid((C + 127) / 128, nsplit, rseg / 64);
+  const dim3 grid(xcd_grid((C + 127) / 128, nsplit, rseg / 64));
   if (trans)
     hipLaunchKernelGGL(grad_tr_kernel<true>, grid, dim3(512), smem, s, Ph, Pl, Q, M, Mp, C, rp, mchunk, segC, rseg,
-                       part);
+                       nsplit, part);
   else
     hipLaunchKernelGGL(grad_tr_kernel<false>, grid, dim3(512), smem, s, Ph, Pl, Q, M, Mp, C, rp, mchunk, segC, rseg,
-                       part);
+                       nsplit, part);
   return hipGetLastError();
 }
 
