@@ -583,6 +583,31 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
 
   // D layout of a 16 x 16 tile: lane holds rows 4 (l >> 4) + v, column l & 15
   float* __restrict__ part = p.ksplit > 1 ? p.part + (int64_t)ksp * p.M * p.Nout : nullptr;
+  if (!part && (p.Nout & 1) == 0) {
+    // bf16 pairs of adjacent columns, one 4-byte store each: lanes l and l ^ 1
+    // (columns c, c ^ 1) swap halves of their 4 rows, so the even lane holds
+    // rows 0-1 and the odd lane rows 2-3 of both columns (same rounding)
+    const bool odd = l & 1;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 a = acc[i][j];
+        const float s0 = odd ? a[0] : a[2], s1 = odd ? a[1] : a[3];
+        const float r0 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s0), 0xB1, 0xF, 0xF, false));
+        const float r1 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s1), 0xB1, 0xF, 0xF, false));
+        const int col = n0 + wn * 64 + 16 * j + (l & 14);
+        const int row = m0 + wm * WM + 16 * i + 4 * (l >> 4) + (odd ? 2 : 0);
+        const uint32_t w0 = odd ? pack_bf16(r0, a[2]) : pack_bf16(a[0], r0);
+        const uint32_t w1 = odd ? pack_bf16(r1, a[3]) : pack_bf16(a[1], r1);
+        if (col < p.Nout) {
+          uint16_t* o = p.out + (int64_t)row * p.Nout + col;
+          if (row < p.M) *reinterpret_cast<uint32_t*>(o) = w0;
+          if (row + 1 < p.M) *reinterpret_cast<uint32_t*>(o + p.Nout) = w1;
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
