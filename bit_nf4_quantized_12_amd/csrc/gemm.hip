@@ -496,7 +496,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmParams p) {
     if (!SPREAD) load_x(kt + 1, st ^ 1, 0, XJ);
     if (KEEP) __builtin_amdgcn_sched_barrier(0);
     next = load_w(kt + 2);
-    if (KEEP) __builtin_amdgcn_sched_barrier(0);
+    if (KEEP) {
+      // `cur` was loaded a step ago and may still be in flight (the previous
+      // step's end waited for its DMA only). Its loads are older than this
+      // step's XJ DMA instructions and NCODE code loads, so vmcnt(XJ + NCODE)
+      // retires them. The compiler does not insert this wait itself: it
+      // counts the mix of LDS-DMA and register loads as out of order, and at
+      // the loop's first step it emitted no wait before reading `cur`.
+      __builtin_amdgcn_s_waitcnt((XJ + NCODE) | (7 << 4) | (15 << 8));
+      __builtin_amdgcn_sched_barrier(0);
+    }
 
     const uint16_t* a_s = sA + st * BM * 64;
     const uint16_t* b_s = sB + st * BN * 64;
