@@ -12,10 +12,12 @@
 // columns of T = X A^T over the whole reduction, float32, written once; the
 // backward's recompute of T runs the same launch, so a saved and a recomputed
 // T are bit-identical), the second streams the weight and adds s T B^T at its
-// epilogue. (A single launch whose first workgroups published T to the others
-// through a counter measured 2-3x slower: while the weight stream saturates
-// HBM, the release, the atomic and the polls each wait behind that traffic,
-// and the handoff took 5-10 us.)
+// epilogue. With more than 8 tokens, extra workgroups of the first launch
+// read the weight ahead of the second (into the Infinity Cache). (A single
+// launch whose first workgroups published T to the others through a counter
+// measured 2-3x slower: while the weight stream saturates HBM, the release,
+// the atomic and the polls each wait behind that traffic, and the handoff
+// took 5-10 us.)
 //
 //  * stream layout: 8 wave64; lane l has weight row c = l & 15 of the
 //    workgroup and slot s = 4 w + (l >> 4) of 32; slot s takes the 64-weight
@@ -195,9 +197,44 @@ __device__ void ft_produce(const FewTokParams& p, int j0, float* red) {
   }
 }
 
-// T = X A^T: workgroup w computes columns w J .. w J + J - 1.
+// Workgroups P .. of the T launch read the stored weight that the next
+// launch streams (codes, then the block constants), 16 bytes per lane, 8
+// loads in flight, and drop the data: the lines land in the Infinity Cache
+// while T's reduction chain, which leaves HBM idle, runs, and the weight
+// stream then reads them from there instead of from HBM.
+constexpr int FT_PF_LOADS = 8;
+__device__ void ft_touch(const uint8_t* base, size_t bytes, int wg, int nwg) {
+  const size_t chunk = (size_t)FT_NT * 16 * FT_PF_LOADS;  // bytes per workgroup round
+  const size_t n16 = bytes / 16;  // whole 16-byte pieces (a shorter tail is left out)
+  if (n16 == 0) return;
+  uint32_t sink = 0;
+  for (size_t c = (size_t)wg * chunk; c < bytes; c += (size_t)nwg * chunk) {
+    uint4 v[FT_PF_LOADS];
+#pragma unroll
+    for (int i = 0; i < FT_PF_LOADS; ++i) {
+      const size_t e = min(c / 16 + (size_t)i * FT_NT + threadIdx.x, n16 - 1);
+      v[i] = reinterpret_cast<const uint4*>(base)[e];
+    }
+#pragma unroll
+    for (int i = 0; i < FT_PF_LOADS; ++i) sink ^= v[i].x;
+  }
+  asm volatile("" ::"v"(sink));
+}
+
+// T = X A^T: workgroup w < P computes columns w J .. w J + J - 1; the
+// others (forward only) read the weight ahead of its stream.
 __global__ __launch_bounds__(FT_NT) void fewtok_t_kernel(FewTokParams p) {
   __shared__ float pred[FT_PM * FT_W];
+  if ((int)blockIdx.x >= p.P) {
+    const int wg = blockIdx.x - p.P, nwg = gridDim.x - p.P;
+    const size_t n = (size_t)p.N * p.K;
+    ft_touch(p.codes, n / 2, wg, nwg);
+    if (p.absmax)
+      ft_touch(reinterpret_cast<const uint8_t*>(p.absmax), (n / 64) * 4, wg, nwg);
+    else
+      ft_touch(p.c2, n / 64, wg, nwg);
+    return;
+  }
   ft_produce(p, blockIdx.x * p.J, pred);
 }
 
@@ -382,7 +419,13 @@ hipError_t launch_fewtok(const uint16_t* X, const uint8_t* codes, const uint8_t*
   ft_producers(R, &p.P, &p.J);
   p.scale = scale;
   p.lv = host_levels(codebook);
-  hipLaunchKernelGGL(fewtok_t_kernel, dim3(p.P), dim3(FT_NT), 0, s, p);
+  // forward with more than 8 tokens: one reading workgroup per 64 KB of the
+  // stored weight, at most 256 beside the T workgroups. (With 8 tokens or
+  // fewer the reading outlasts T's own chain and the stream gains less than
+  // that: measured slower at M = 1, 4-7 % faster at M = 16.)
+  const size_t wbytes = (size_t)N * K / 2;
+  const int npf = Y && M > 8 ? (int)std::min<size_t>(256, (wbytes + 65535) / 65536) : 0;
+  hipLaunchKernelGGL(fewtok_t_kernel, dim3(p.P + npf), dim3(FT_NT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !Y) return e;
   const dim3 grid((N + 15) / 16);
