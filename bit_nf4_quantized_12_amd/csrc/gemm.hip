@@ -17,11 +17,12 @@
 // step grows with BN and the MFMA work with BM x BN, so the 512 x 128 tile
 // halves the unpacking per MFMA at the same LDS read volume per step. LDS
 // holds two stages of the activation tile and of the weight tile (bf16,
-// 128 or 160 KB in all, 16-byte chunks XOR-swizzled per row so MFMA operand
+// 64, 128 or 160 KB in all, 16-byte chunks XOR-swizzled per row so MFMA operand
 // reads are conflict free). The activation tile is streamed global -> LDS
 // by LDS-DMA, no registers involved: 512-row tiles issue it as buffer loads
 // spread over the first half-step's MFMAs, the others as global loads at
-// the top of the step.
+// the top of the step. 512-row tiles also touch the activation band in L2
+// three steps ahead of that DMA.
 //
 // Weight tiles are unpacked in registers: each thread owns BN / 8 codes of
 // one block per step (a quarter or half of it), the block's 16-entry table
@@ -33,7 +34,8 @@
 //
 // Workgroups are ordered so that each XCD (workgroup id mod 8) owns a
 // contiguous band of output tiles: the activation rows and weight columns
-// it streams stay in that XCD's L2.
+// it streams stay in that XCD's L2. Outputs are stored as bf16 pairs of
+// adjacent columns (or float32 partials when the reduction is split).
 #include "launch.hpp"
 
 namespace qlora {
