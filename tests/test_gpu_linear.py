@@ -79,6 +79,9 @@ def test_single_linear_256_r8():
     (200, 96, 1024, 2), (8, 136, 256, 100), (16, 72, 128, 256),
     # few-token T projection with a partial pass of 9..15 tokens
     (11, 260, 448, 24), (13, 520, 1024, 64),
+    # more than 8 tokens with a weight whose block constants fill less than 16 bytes (the read-ahead
+    # workgroups of the T launch skip that part)
+    (9, 3, 64, 2), (16, 1, 64, 1),
     # from 1024 tokens the GEMM runs 512 x 128 tiles: ragged M, N and reductions there too
     (1030, 200, 384, 33), (1500, 1000, 640, 64), (2048, 131, 64, 256), (1100, 96, 1024, 2),
     # input gradient whose last 128-column tile is half past K (quads of lanes whose block lies
